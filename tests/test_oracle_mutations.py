@@ -1,0 +1,88 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of oracle.c (a flipped comparison, a
+wrong row or uniform index, a transposed ratio, a dropped temperature, a
+wrong search direction ...), compiles the copy with gcc, and runs the pins
+of the affected function against it.  At least one pin must fail for every
+planted mistake; the shipped oracle passes them all.  Mistakes are planted
+only in the CPU oracle and only in temporary copies.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_greedy as G
+import test_oracle_rejection as R
+import test_oracle_tree_ngram as TN
+from conftest import golden
+
+TAU = golden("tau_values.json")["cases"]
+
+GREEDY_PINS = [G.test_worked_example, G.test_all_accepted_plus_one,
+               G.test_argmax_matches_numpy_with_ties, G.test_draft_len_and_flags,
+               lambda o: G.test_greedy_identity_planted_proposer(o, 0.9),
+               lambda o: G.test_tau_closed_form(o, TAU[0])]
+REJECTION_PINS = [R.test_worked_example_sampling_form, R.test_flags_and_draft_len,
+                  R.test_one_hot_target_is_greedy,
+                  R.test_probabilities_match_scipy_softmax_with_temperature,
+                  lambda o: R.test_output_distribution_chisquare_v8(o, 1),
+                  lambda o: R.test_output_distribution_chisquare_v8(o, 3),
+                  R.test_identical_draft_accepts_everything, R.test_one_hot_draft_accepts_with_p]
+TREE_PINS = [TN.test_tree_single_node, TN.test_tree_equal_depth_tie_lowest_id,
+             TN.test_chain_tree_is_greedy,
+             TN.test_random_trees_brute_force]
+NGRAM_PINS = [TN.test_ngram_overlap_short_and_ragged, TN.test_ngram_planted_copy,
+              TN.test_ngram_exhaustive_ternary]
+
+MUTANTS = [
+    ("argmax keeps the last maximum", "if (x > bv) {", "if (x >= bv) {", GREEDY_PINS),
+    ("greedy compares with the next row",
+     "draft[(size_t)b * K + n] == t[n])", "draft[(size_t)b * K + n] == t[n + 1])", GREEDY_PINS),
+    ("bonus from the previous row", "e = t[n];", "e = t[n > 0 ? n - 1 : 0];", GREEDY_PINS),
+    ("temperature dropped from the normaliser",
+     "Z += exp(orc_widen(row, dtype, v) / T - M);", "Z += exp(orc_widen(row, dtype, v) - M);",
+     REJECTION_PINS),
+    ("ratio transposed", "ratio = qi > 0.0 ? pi / qi : INFINITY;",
+     "ratio = pi > 0.0 ? qi / pi : INFINITY;", REJECTION_PINS),
+    ("accept test reversed", "if (ui < ratio)", "if (ui > ratio)", REJECTION_PINS),
+    ("residual sign flipped", "double d = P[v] - Q[v];", "double d = Q[v] - P[v];",
+     REJECTION_PINS),
+    ("residual not clipped at zero", "r[v] = d > 0.0 ? d : 0.0;", "r[v] = d;", REJECTION_PINS),
+    ("final sample uses the first uniform", "double thr = (double)ub[K] * S;",
+     "double thr = (double)ub[0] * S;", REJECTION_PINS),
+    ("no stop at the first rejection", "stopped = 1;", "stopped = 0;", REJECTION_PINS),
+    ("tree checks the node's own row", "acc[j] = acc[p] && tok[j] == t[p];",
+     "acc[j] = acc[p] && tok[j] == t[j];", TREE_PINS),
+    ("tree ignores the parent's acceptance", "acc[j] = acc[p] && tok[j] == t[p];",
+     "acc[j] = tok[j] == t[p];", TREE_PINS),
+    ("tree ties go to the largest id", "if (acc[j] && depth[j] > bestd) {",
+     "if (acc[j] && depth[j] >= bestd) {", TREE_PINS),
+    ("n-gram takes the earliest occurrence", "for (int64_t s = L - n - 1; s >= 0; --s) {",
+     "for (int64_t s = 0; s <= L - n - 1; ++s) {", NGRAM_PINS),
+    ("n-gram tries the shortest length first",
+     "for (int32_t n = n_max; n >= n_min && got_n == 0; --n) {",
+     "for (int32_t n = n_min; n <= n_max && got_n == 0; ++n) {", NGRAM_PINS),
+    ("n-gram copies from the match start", "pr[k] = c[got_s + got_n + k];",
+     "pr[k] = c[got_s + k];", NGRAM_PINS),
+    ("n-gram lets the suffix match itself", "for (int64_t s = L - n - 1; s >= 0; --s) {",
+     "for (int64_t s = L - n; s >= 0; --s) {", NGRAM_PINS),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new, pins):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert src.count(old) == 1, "mutation anchor must be unique: %r" % old
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    so = oracle.compile_source(str(mut), str(tmp_path / "liboracle_mut.so"))
+    m = oracle.Oracle(so)
+    failed = []
+    for pin in pins:
+        try:
+            pin(m)
+        except AssertionError:
+            failed.append(getattr(pin, "__name__", "pin"))
+            break
+    assert failed, "no pin caught the planted mistake: %s" % name

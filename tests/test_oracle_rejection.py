@@ -1,0 +1,192 @@
+"""Pins for the oracle's rejection-sampling verification (runs on the CPU).
+
+The pages state that rejection sampling keeps the target distribution
+(vLLM features 03, '1. principle', citing Leviathan et al. and Chen et al.)
+and name it as the usual verifier (Arctic blog, 'what is speculative
+decoding').  These tests check the oracle against consequences of that rule
+that do not depend on the oracle's own code: the output distribution
+(chi-square at V = 8), the per-position acceptance probability
+sum_x min(p(x), q(x)), special cases that reduce to greedy verification or
+to a point mass, scipy's softmax, and the worked example in sampling form.
+"""
+import numpy as np
+import pytest
+from scipy import special, stats
+
+from conftest import golden
+
+NEG = np.float32(-1.0e4)   # exp(-1e4 - M) is exactly 0 in fp64
+
+
+def _softmax64(logits32):
+    return special.softmax(np.asarray(logits32, np.float64), axis=-1)
+
+
+def _sample_rows(rng, probs, n):
+    """n draws from each row of probs (inverse CDF in numpy)."""
+    c = np.cumsum(probs, axis=-1)
+    c[:, -1] = 1.0
+    u = rng.random((n, probs.shape[0]))
+    return np.stack([np.searchsorted(c[i], u[:, i], side="right") for i in range(probs.shape[0])],
+                    axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_output_distribution_chisquare_v8(orc, K):
+    """Given position j is reached, the emitted token is distributed as the
+    target's p_j; the accept frequency at position i is sum_x min(p_i, q_i)."""
+    rng = np.random.default_rng(100 + K)
+    V, T = 8, 200_000
+    p = rng.dirichlet(np.ones(V), size=K + 1)
+    q = rng.dirichlet(np.ones(V), size=K)
+    tl = np.log(p).astype(np.float32)
+    dl = np.log(q).astype(np.float32)
+    p_eff = _softmax64(tl)          # what the fp32 logits really encode
+    q_eff = _softmax64(dl)
+    target = np.broadcast_to(tl, (T, K + 1, V)).copy()
+    draftl = np.broadcast_to(dl, (T, K, V)).copy()
+    x = _sample_rows(rng, q_eff, T)
+    u = rng.random((T, K + 1), dtype=np.float32)
+    out = orc.verify_rejection(target, draftl, x, u)
+    n = out["accepted"]
+    for j in range(K + 1):
+        reached = n >= j
+        tok = out["emitted"][reached, j]
+        counts = np.bincount(tok, minlength=V)
+        assert stats.chisquare(counts, p_eff[j] * reached.sum()).pvalue > 1e-3
+    for i in range(K):
+        reached = n >= i
+        acc = (n[reached] > i).astype(np.float64)
+        beta = np.minimum(p_eff[i], q_eff[i]).sum()
+        assert abs(acc.mean() - beta) < 4 * np.sqrt(beta * (1 - beta) / reached.sum())
+    # reported probabilities are the softmax values at the drafted ids
+    np.testing.assert_allclose(out["p_draft"], p_eff[np.arange(K), x], rtol=1e-12)
+    np.testing.assert_allclose(out["q_draft"], q_eff[np.arange(K), x], rtol=1e-12)
+
+
+def test_probabilities_match_scipy_softmax_with_temperature(orc):
+    """p_i(x_i), q_i(x_i) equal scipy.special.softmax(logits / T) at x_i."""
+    rng = np.random.default_rng(7)
+    B, K, V = 6, 4, 333
+    for T in (0.5, 1.0, 1.7):
+        tl = (rng.standard_normal((B, K + 1, V)) * 3).astype(np.float32)
+        dl = (rng.standard_normal((B, K, V)) * 3).astype(np.float32)
+        x = rng.integers(0, V, (B, K)).astype(np.int32)
+        u = rng.random((B, K + 1), dtype=np.float32)
+        out = orc.verify_rejection(tl, dl, x, u, temperature=T)
+        ps = special.softmax(tl.astype(np.float64) / T, axis=-1)
+        qs = special.softmax(dl.astype(np.float64) / T, axis=-1)
+        bi, ki = np.meshgrid(np.arange(B), np.arange(K), indexing="ij")
+        np.testing.assert_allclose(out["p_draft"], ps[bi, ki, x], rtol=1e-12)
+        np.testing.assert_allclose(out["q_draft"], qs[bi, ki, x], rtol=1e-12)
+
+
+def test_identical_draft_accepts_everything(orc):
+    """q = p: p/q = 1 > u, so every draft is accepted and the bonus ~ p_K."""
+    rng = np.random.default_rng(8)
+    V, K, T = 8, 3, 100_000
+    tl = np.log(rng.dirichlet(np.ones(V), size=K + 1)).astype(np.float32)
+    target = np.broadcast_to(tl, (T, K + 1, V)).copy()
+    draftl = target[:, :K, :].copy()
+    x = _sample_rows(rng, _softmax64(tl[:K]), T)
+    u = rng.random((T, K + 1), dtype=np.float32)
+    out = orc.verify_rejection(target, draftl, x, u)
+    assert (out["accepted"] == K).all()
+    counts = np.bincount(out["emitted"][:, K], minlength=V)
+    assert stats.chisquare(counts, _softmax64(tl[K]) * T).pvalue > 1e-3
+
+
+def test_one_hot_target_is_greedy(orc):
+    """A one-hot target p makes rejection sampling deterministic: a draft is
+    accepted iff it is the target's token, and the residual after a
+    rejection is a point mass on that token -- greedy verification."""
+    rng = np.random.default_rng(9)
+    B, K, V = 400, 4, 50
+    t = rng.integers(0, V, (B, K + 1))
+    tl = np.full((B, K + 1, V), NEG, np.float32)
+    np.put_along_axis(tl, t[..., None], 0.0, axis=-1)
+    dl = rng.standard_normal((B, K, V)).astype(np.float32)
+    x = np.where(rng.random((B, K)) < 0.7, t[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    rej = orc.verify_rejection(tl, dl, x, u)
+    gre = orc.verify_greedy(tl, x)
+    assert np.array_equal(rej["accepted"], gre["accepted"])
+    assert np.array_equal(rej["emitted"], gre["emitted"])
+
+
+def test_one_hot_draft_accepts_with_p(orc):
+    """q one-hot at x gives p/q = p(x): accepted with probability p(x)."""
+    rng = np.random.default_rng(10)
+    V, T = 8, 200_000
+    tl = np.log(rng.dirichlet(np.ones(V), size=2)).astype(np.float32)
+    x0 = 3
+    dl = np.full((1, V), NEG, np.float32)
+    dl[0, x0] = 0.0
+    target = np.broadcast_to(tl, (T, 2, V)).copy()
+    draftl = np.broadcast_to(dl, (T, 1, V)).copy()
+    x = np.full((T, 1), x0, np.int32)
+    u = rng.random((T, 2), dtype=np.float32)
+    out = orc.verify_rejection(target, draftl, x, u)
+    pa = _softmax64(tl[0])[x0]
+    freq = out["accepted"].mean()
+    assert abs(freq - pa) < 4 * np.sqrt(pa * (1 - pa) / T)
+    # after a rejection the residual max(0, p - q) excludes x0 entirely
+    rej = out["accepted"] == 0
+    assert not (out["emitted"][rej, 0] == x0).any()
+
+
+def test_worked_example_sampling_form(orc):
+    """Arctic blog, 'a simple example', with a sampling verifier: the target
+    favours 13 and 578 (ratio >= 1: accepted for any u); at the third
+    position p = {7301: 0.1, 21747: 0.9}, q = {7301: 0.5, 6: 0.5} and
+    u = 0.9 > p/q = 0.2 rejects 7301; the residual max(0, p - q) is a point
+    mass on 21747, which is emitted whatever the final uniform."""
+    g = golden("worked_example.json")
+    V = g["vocab_for_test"]
+    d = g["drafts"]
+
+    def row(mass):
+        r = np.full(V, NEG, np.float32)
+        for k, v in mass.items():
+            r[k] = np.log(v)
+        return r
+    tl = np.stack([row({d[0]: 0.9, 5: 0.1}), row({d[1]: 0.8, 5: 0.2}),
+                   row({d[2]: 0.1, g["target_token"]: 0.9}), row({1: 1.0})])[None]
+    dl = np.stack([row({d[0]: 0.5, 6: 0.5}), row({d[1]: 0.4, 6: 0.6}),
+                   row({d[2]: 0.5, 6: 0.5})])[None]
+    for ufin in (0.0, 0.5, 0.999):
+        u = np.array([[0.99, 0.99, 0.9, ufin]], np.float32)
+        out = orc.verify_rejection(tl, dl, np.array([d], np.int32), u)
+        assert out["accepted"][0] == 2
+        assert out["emitted"][0].tolist() == g["accepted_drafts"] + [g["target_token"], -1]
+        assert out["p_draft"][0, 2] == pytest.approx(0.1, rel=1e-6)
+        assert out["q_draft"][0, 2] == pytest.approx(0.5, rel=1e-6)
+
+
+def test_flags_and_draft_len(orc):
+    """Out-of-range draft ids are rejected (flagged); draft_len 0 samples the
+    bonus from p_0; lengths outside [0, K] are clamped and flagged; a
+    near-tie accept test is reported."""
+    rng = np.random.default_rng(11)
+    B, K, V = 4, 3, 16
+    tl = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    dl = tl[:, :K, :].copy()                  # q = p: valid drafts always accepted
+    x = rng.integers(0, V, (B, K)).astype(np.int32)
+    x[1, 1] = -3
+    u = rng.random((B, K + 1), dtype=np.float32)
+    dlen = np.array([0, 3, 7, 2], np.int32)
+    out = orc.verify_rejection(tl, dl, x, u, draft_len=dlen)
+    assert out["accepted"].tolist() == [0, 1, 3, 2]
+    assert out["flags"].tolist() == [0, orc.FLAG_DRAFT_OOR, orc.FLAG_BAD_LEN, 0]
+    assert (out["emitted"][0, 1:] == -1).all()
+    assert out["p_draft"][1, 1] == 0.0 and out["q_draft"][1, 1] == 0.0
+    # draft_len 0: the emitted token is a sample of p_0 with u[b][K]
+    c = np.cumsum(_softmax64(tl[0, 0]))
+    assert out["emitted"][0, 0] == int(np.searchsorted(c, u[0, K] * c[-1], side="right"))
+    # a uniform planted just below p/q is flagged as an accept tie
+    tl2 = np.log(np.array([[[0.3, 0.7], [0.5, 0.5]]])).astype(np.float32)
+    dl2 = np.log(np.array([[[0.6, 0.4]]])).astype(np.float32)
+    ratio = _softmax64(tl2[0, 0])[0] / _softmax64(dl2[0, 0])[0]
+    u2 = np.array([[np.nextafter(np.float32(ratio), np.float32(0)), 0.5]], np.float32)
+    out2 = orc.verify_rejection(tl2, dl2, np.array([[0]], np.int32), u2)
+    assert out2["accept_tie"][0]
