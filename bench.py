@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+
+  n-gram propose   64 contexts x 8192 Zipf(1.1) ids, planted copies, n 5..2, K 8
+  rejection verify B 64, K 5, V 128256, bf16 target N(0,2) / draft +N(0,0.5), T 1
+  greedy verify    B 256, K 8, V 151936, bf16 N(0,2), planted acceptance 0.6
+  tree verify      B 32, 64-node trees, V 128256, bf16 N(0,2)
+
+Inputs are resident in HBM before the timed region; the four inputs together
+(about 1.4 GB) exceed the 256 MB last-level cache, so every step reads its
+logits from HBM.  `value` is verified positions per second over the whole
+step (384 + 2304 + 2048 = 4736 positions per step).  Each call is bracketed
+by HIP events on the stream the kernels run on; the dominant kernel's
+average gives the roofline figure.  The CPU oracle runs the same step on the
+host cores beside it (cpu_baseline).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified positions/s + HBM GB/s (% of peak) at V=128k; n-gram proposals/s"
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "greedy": ["proposal_sv_verify_amd/csrc/argmax_verify.hip",
+               "proposal_sv_verify_amd/csrc/sv_device.hpp",
+               "proposal_sv_verify_amd/csrc/sv_kernels.hpp"],
+}
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def make_inputs():
+    from proposal_sv_verify_amd import workloads as W
+    t0 = time.time()
+    ng = W.ngram_workload(64, 8192, seed=W.seed_for(2))
+    rj = W.rejection_workload(**W.REJECTION, seed=W.seed_for(3))
+    gr = W.greedy_workload(256, 8, 151936, "bf16", 2.0, (0.6,), seed=W.seed_for(4))
+    tr = W.tree_workload(**W.TREE, seed=W.seed_for(5))
+    log("inputs generated in %.1f s" % (time.time() - t0))
+    return ng, rj, gr, tr
+
+
+def ngram_bytes(out, lengths, n_max):
+    """Positions the backward scan must examine: from the end of the context
+    down to the start of the most recent full-length match, or to the start
+    of the context when there is none (4 bytes per position)."""
+    mn, mp = out["match_n"], out["match_pos"]
+    stop = np.where(mn == n_max, mp, 0)
+    return int(4 * (lengths.astype(np.int64) - stop).sum())
+
+
+def run_gpu(args, ng, rj, gr, tr):
+    import torch
+    import proposal_sv_verify_amd as sv
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = dict(
+        ng_tok=to_dev(ng["tokens"]), ng_len=to_dev(ng["lengths"]),
+        rj_t=to_dev(rj["target"]), rj_d=to_dev(rj["draft_logits"]), rj_x=to_dev(rj["draft"]),
+        rj_u=to_dev(rj["uniforms"]),
+        gr_l=to_dev(gr["logits"]), gr_x=to_dev(gr["drafts"][0.6]),
+        tr_l=to_dev(tr["logits"]), tr_p=to_dev(tr["parent"]), tr_t=to_dev(tr["token"]),
+    )
+    torch.cuda.synchronize()
+    calls = [
+        ("ngram", sv.prepare_ngram(d["ng_tok"], d["ng_len"], 2, 5, 8)),
+        ("rejection", sv.prepare_rejection(d["rj_t"], d["rj_d"], d["rj_x"], d["rj_u"], 1.0)),
+        ("greedy", sv.prepare_greedy(d["gr_l"], d["gr_x"])),
+        ("tree", sv.prepare_tree(d["tr_l"], d["tr_p"], d["tr_t"])),
+    ]
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record()
+        for j, (_, c) in enumerate(calls):
+            c()
+            e[j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)])) * 1e3
+           for j, (name, _) in enumerate(calls)}
+    outs = {name: {k: v.cpu().numpy() for k, v in c.out.items()} for name, c in calls}
+    return wall, per, outs, d
+
+
+def ngram_bandwidth_mode(args):
+    """The n-gram generator at 16384 contexts (512 MiB) in one call."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    from proposal_sv_verify_amd import workloads as W
+
+    wl = W.ngram_workload(16384, 8192, seed=W.seed_for(2, salt=1))
+    dev = torch.device("cuda:0")
+    tok = torch.from_numpy(wl["tokens"]).to(dev)
+    lens = torch.from_numpy(wl["lengths"]).to(dev)
+    call = sv.prepare_ngram(tok, lens, 2, 5, 8)
+    for _ in range(3):
+        call()
+    reps = 20
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for r in range(reps):
+        call()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)])) * 1e3
+    out = {k: v.cpu().numpy() for k, v in call.out.items()}
+    nbytes = ngram_bytes(out, wl["lengths"], 5)
+    gbs = nbytes / us / 1e3
+    return dict(contexts=16384, context_len=8192, us_per_call=round(us, 2),
+                proposals_per_s=round(16384 / us * 1e6, 1), algorithmic_bytes=nbytes,
+                gb_per_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+
+def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
+    """The oracle, as it stands, on the host cores: whole steps (all four
+    calls, every sequence), sequences spread over a thread pool, for at
+    least `seconds` of wall time.  Also reports whether it agrees with the
+    GPU step's outputs."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    pool = ThreadPoolExecutor(threads)
+
+    def split(B):
+        n = min(B, threads * 4)
+        edges = np.linspace(0, B, n + 1).astype(int)
+        return [(a, b) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+    def merge(parts):
+        return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+
+    def step():
+        o = {}
+        o["ngram"] = merge(list(pool.map(lambda ab: oracle.ngram_propose(
+            ng["tokens"][ab[0]:ab[1]], ng["lengths"][ab[0]:ab[1]], 2, 5, 8), split(64))))
+        o["rejection"] = merge(list(pool.map(lambda ab: oracle.verify_rejection(
+            rj["target"][ab[0]:ab[1]], rj["draft_logits"][ab[0]:ab[1]], rj["draft"][ab[0]:ab[1]],
+            rj["uniforms"][ab[0]:ab[1]], 1.0), split(64))))
+        o["greedy"] = merge(list(pool.map(lambda ab: oracle.verify_greedy(
+            gr["logits"][ab[0]:ab[1]], gr["drafts"][0.6][ab[0]:ab[1]]), split(256))))
+        o["tree"] = merge(list(pool.map(lambda ab: oracle.verify_tree(
+            tr["logits"][ab[0]:ab[1]], tr["parent"][ab[0]:ab[1]], tr["token"][ab[0]:ab[1]]),
+            split(32))))
+        return o
+
+    t0 = time.perf_counter()
+    n = 0
+    ref = None
+    while True:
+        ref = step()
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    pool.shutdown()
+    parity = None
+    if gpu_outs is not None:
+        g = gpu_outs
+        ok = all(np.array_equal(g["greedy"][k], ref["greedy"][k]) for k in ("accepted", "emitted"))
+        ok &= all(np.array_equal(g["tree"][k], ref["tree"][k]) for k in ("accepted", "path", "emitted"))
+        ok &= all(np.array_equal(g["ngram"][k], ref["ngram"][k])
+                  for k in ("proposal", "proposal_len", "match_n", "match_pos"))
+        r = ref["rejection"]
+        same = (g["rejection"]["accepted"] == r["accepted"]) & \
+               (g["rejection"]["emitted"] == r["emitted"]).all(axis=1)
+        tie = r["accept_tie"] | r["sample_tie"]
+        ok &= bool((same | tie).all())
+        parity = dict(all_match=bool(ok), rejection_flagged_ties=int(tie.sum()),
+                      rejection_mismatches=int((~same).sum()))
+    return dict(value=round(4736 * n / el, 1), unit="verified positions/s", cores=threads,
+                kind="oracle",
+                sample="%d full step(s): all four calls over every sequence (%.1f s)" % (n, el)), parity
+
+
+def load_traffic(name, per_launch_us_unused=None):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if the
+    kernel's sources are unchanged since they were taken."""
+    path = os.path.join(PROFILES, "%s_counters.json" % name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_hash") != source_hash(KERNEL_SOURCES[name]):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-bandwidth-mode", action="store_true",
+                    help="skip the 16384-context n-gram measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    ng, rj, gr, tr = make_inputs()
+    wall, per, outs, _ = run_gpu(args, ng, rj, gr, tr)
+    K = args.steps
+    ms_step = wall / K * 1e3
+    positions = 64 * 6 + 256 * 9 + 32 * 64
+
+    algo = {
+        "rejection": 64 * 6 * 128256 * 2 + 64 * 5 * 128256 * 2,
+        "greedy": 256 * 9 * 151936 * 2,
+        "tree": 32 * 64 * 128256 * 2,
+        "ngram": ngram_bytes(outs["ngram"], ng["lengths"], 5),
+    }
+    units = {"rejection": 384, "greedy": 2304, "tree": 2048, "ngram": 64}
+    kernels = {}
+    for name, us in per.items():
+        gbs = algo[name] / us / 1e3
+        kernels[name] = dict(us_per_call=round(us, 2), algorithmic_bytes=algo[name],
+                             gb_per_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
+                             units_per_s=round(units[name] / us * 1e6, 1),
+                             unit="proposals" if name == "ngram" else "positions")
+    dom = max(("rejection", "greedy", "tree"), key=lambda k: per[k])
+    achieved = algo[dom] / per[dom] / 1e3
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4),
+                    traffic=load_traffic(dom) if dom in KERNEL_SOURCES else None,
+                    kernel=dom, algorithmic_bytes_per_launch=algo[dom],
+                    avg_launch_us=round(per[dom], 2))
+
+    result = dict(metric=METRIC, value=round(positions * K / wall, 1), unit="verified positions/s",
+                  n_gpus=1, steps=K, warmup=args.warmup, ms_per_step=round(ms_step, 4),
+                  higher_is_better=True, scaling="weak", vs_baseline=None,
+                  dtype="bf16 logits; f32 exp, f64 sums", data="synthetic",
+                  config=dict(workload="one verify+propose pass: ngram B64 L8192 n5..2 K8; "
+                                       "rejection B64 K5 V128256 bf16 T1; greedy B256 K8 V151936 "
+                                       "bf16 alpha0.6; tree B32 N64 V128256 bf16",
+                              positions_per_step=positions, proposals_per_step=64),
+                  roofline=roofline, kernels=kernels)
+    if not args.no_bandwidth_mode:
+        result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
+    if not args.no_cpu:
+        cb, parity = cpu_baseline(ng, rj, gr, tr, args.cpu_seconds, outs)
+        result["cpu_baseline"] = cb
+        result["parity"] = parity
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the data-parallel hot path of
+ * speculative decoding on AMD Instinct MI355X (gfx950):
+ *
+ *   sv_verify_greedy     greedy verification of K drafts per sequence
+ *   sv_verify_rejection  rejection-sampling verification (target p, draft q)
+ *   sv_verify_tree       greedy verification of a candidate tree
+ *   sv_ngram_propose     n-gram prompt-lookup drafting
+ *
+ * Pages this follows (section names as the pages give them):
+ *  [Arctic]   "Fastest Speculative Decoding in vLLM with Arctic Inference and
+ *             Arctic Training" (Snowflake; Chinese repost): proposer / scorer
+ *             / verifier split ("what is speculative decoding"), the worked
+ *             step ("a simple example"), greedy verification by a custom
+ *             kernel ("inference pipeline optimisation").
+ *  [Handbook] LLM Inference Handbook, "speculative decoding": the
+ *             draft-verify loop ("how it works"), candidate trees ("Medusa"),
+ *             prompt lookup ("N-gram").
+ *  [vLLM-03]  "vLLM features 03: speculative decoding" (ttlab): stop at the
+ *             first wrong draft and substitute the target's token; rejection
+ *             sampling at T > 0 ("1. principle"); prompt_lookup_min/max
+ *             ("2. draft methods"); no match means no draft ("3-1").
+ * The rejection rule is Leviathan et al. / Chen et al., which [vLLM-03]
+ * cites: accept draft x with probability min(1, p(x)/q(x)); after a
+ * rejection sample from max(0, p - q) normalised.
+ *
+ * Conventions for every call
+ *  - All array arguments are DEVICE pointers (hipMalloc'd or equivalent),
+ *    row-major, owned by the caller, which must keep them alive until the
+ *    work enqueued on `stream` has completed.  The library allocates and
+ *    frees nothing inside these calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues kernels and returns; outputs are valid after
+ *    the stream reaches that point.  No call synchronises.
+ *  - Logits are fp32 (SV_F32) or bf16 (SV_BF16, raw IEEE bf16 bits) with
+ *    `row_stride` elements between consecutive rows (row_stride >= V); the
+ *    base pointer must be aligned to the element size.
+ *  - Scalars and pointers are validated on the host BEFORE anything is
+ *    enqueued; on error the call returns a non-zero status, writes nothing
+ *    and sv_last_error_message() explains.  Malformed DATA found on the
+ *    device has a defined result and sets a bit in flags[b] (flags may be
+ *    NULL): see SV_FLAG_*.
+ *  - Workspaces hold per-row partial results and arrival counters.  Size
+ *    one with the matching sv_*_workspace_bytes(); it must be 16-byte
+ *    aligned and ZERO-FILLED before its first use (hipMemset / torch.zeros).
+ *    Every completed call leaves the whole workspace all-zero again, so one
+ *    workspace serves any sequence of calls of any kind and size without
+ *    clearing.  Calls that share a workspace must be ordered on one stream;
+ *    calls running concurrently need their own.
+ *  - argmax ties resolve to the LOWEST token id (the numpy / torch rule);
+ *    -0.0 and +0.0 compare equal.  Rows must be free of NaN.
+ *  - The device must be gfx950 (else SV_ERR_UNSUPPORTED).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+/* status codes */
+#define SV_OK 0
+#define SV_ERR_INVALID_ARG 1   /* a scalar or a required pointer is invalid */
+#define SV_ERR_UNSUPPORTED 2   /* not a gfx950 device, or a size above a documented limit */
+#define SV_ERR_WORKSPACE 3     /* workspace missing, too small or misaligned */
+#define SV_ERR_HIP 4           /* a HIP runtime call or launch failed */
+
+/* logit element types */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* per-sequence data flags (flags[b], written by every call that takes flags) */
+#define SV_FLAG_DRAFT_OOR 1u   /* a draft or tree-node token id outside [0, V):
+                                  it never matches / is rejected */
+#define SV_FLAG_BAD_LEN 2u     /* draft_len outside [0, K] (clamped to it), or an
+                                  n-gram context length outside [0, ctx_stride]
+                                  (treated as empty) */
+#define SV_FLAG_BAD_PARENT 4u  /* tree parent[j] outside [0, j) for j >= 1 (node
+                                  never accepted), or parent[0] != -1 (ignored) */
+
+/* size limits (SV_ERR_UNSUPPORTED beyond them) */
+#define SV_MAX_V (1 << 30)          /* vocabulary */
+#define SV_MAX_TREE_NODES 1024      /* N of sv_verify_tree */
+#define SV_MAX_NGRAM 31             /* n_max of sv_ngram_propose */
+#define SV_MAX_CONTEXT (1 << 26)    /* n-gram context length / ctx_stride */
+#define SV_MAX_PROPOSAL 4096        /* K of sv_ngram_propose */
+#define SV_MAX_DRAFTS 4096          /* K of the verifiers */
+
+int sv_abi_version(void);
+const char *sv_status_string(int status);
+/* Detail of the last non-OK status returned on the calling thread. */
+const char *sv_last_error_message(void);
+
+/*
+ * Launch tuning of the row-streaming kernels (process-wide, not
+ * thread-safe; a value <= 0 restores the default).  Rows are cut into
+ * segments so that a call launches about SV_TUNE_TARGET_WORKGROUPS
+ * workgroups (default 2048: eight per compute unit) without segments
+ * shorter than SV_TUNE_MIN_SEGMENT_BYTES (default 32768).  Workspace sizes
+ * follow the current setting: query them after changing it.
+ */
+#define SV_TUNE_TARGET_WORKGROUPS 1
+#define SV_TUNE_MIN_SEGMENT_BYTES 2
+int sv_set_tuning(int32_t key, int64_t value);
+
+/*
+ * sv_verify_greedy -- [Arctic] "inference pipeline optimisation" (accept
+ * only drafts equal to the greedy choice), [Handbook] "how it works"
+ * (longest agreeing prefix h, the target supplies token h+1), [vLLM-03]
+ * "1. principle".  Per sequence b:
+ *   t_i = argmax_v logits[b][i][v]            for i = 0 .. len
+ *   n   = first i < len with draft[b][i] != t_i (else len)
+ *   accepted[b] = n;  emitted[b] = draft[b][0..n) ++ [t_n], -1 padded
+ * where len = draft_len[b] clamped to [0, K] (K when draft_len is NULL).
+ *
+ *   logits     [B][K+1][row_stride]  row i scores the token after draft i-1
+ *   draft      [B][K] int32
+ *   draft_len  [B] int32 or NULL
+ *   accepted   [B] int32               (out)
+ *   emitted    [B][K+1] int32          (out)
+ *   argmax_out [B][K+1] int32 or NULL  (out; rows past len are not read
+ *                                       and report -1)
+ *   flags      [B] uint32 or NULL      (out)
+ *   stats      int64[3 + K] or NULL    (accumulated, never reset:
+ *              [0] accepted total, [1] drafted total, [2] emitted total,
+ *              [3 + i] sequences whose draft i was accepted)
+ * Limits: 1 <= B, 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= SV_MAX_V.
+ */
+size_t sv_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V);
+int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
+                     const int32_t *draft, const int32_t *draft_len,
+                     int32_t B, int32_t K, int32_t V,
+                     int32_t *accepted, int32_t *emitted, int32_t *argmax_out,
+                     uint32_t *flags, int64_t *stats,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_verify_rejection -- Leviathan / Chen rejection sampling ([vLLM-03]
+ * "1. principle"; [Arctic] "what is speculative decoding").  Per sequence:
+ *   p_i = softmax(target[b][i] / T), q_i = softmax(draft_logits[b][i] / T)
+ *   for i < len: accept x_i = draft[b][i] iff u[b][i] < p_i(x_i) / q_i(x_i)
+ *                (q_i(x_i) = 0 accepts; an id outside [0, V) is rejected);
+ *                stop at the first rejection; n = number accepted
+ *   final token y: n < len -> inverse-CDF sample, in increasing token id,
+ *                  of r = max(0, p_n - q_n) with u[b][K] (r = p_n if it sums
+ *                  to 0); n = len -> the same over r = p_n (the bonus).
+ *   accepted[b] = n;  emitted[b] = x_0 .. x_{n-1}, y, -1 padded.
+ *
+ *   target_logits [B][K+1][row_stride], draft_logits [B][K][row_stride]
+ *                 (same dtype and row_stride)
+ *   draft      [B][K] int32, draft_len [B] int32 or NULL
+ *   uniforms   [B][K+1] fp32 in [0, 1): K accept tests, then the final sample
+ *   temperature  finite, > 0
+ *   accepted [B], emitted [B][K+1] int32 (out)
+ *   p_draft, q_draft [B][K] fp32 or NULL (out: p_i(x_i), q_i(x_i) for
+ *              i < len with a valid id, else 0)
+ *   flags, stats as for sv_verify_greedy.
+ * Arithmetic: exp in fp32 per element, every sum, normaliser, ratio and CDF
+ * in fp64; p_i(x_i), q_i(x_i) use fp64 exp.  Decisions agree with an fp64
+ * evaluation except within a rounding band of a tie.
+ * Limits: 1 <= B, 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= SV_MAX_V.
+ */
+size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V);
+int sv_verify_rejection(const void *target_logits, const void *draft_logits,
+                        int32_t dtype, int64_t row_stride,
+                        const int32_t *draft, const int32_t *draft_len,
+                        const float *uniforms, float temperature,
+                        int32_t B, int32_t K, int32_t V,
+                        int32_t *accepted, int32_t *emitted,
+                        float *p_draft, float *q_draft,
+                        uint32_t *flags, int64_t *stats,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_verify_tree -- [Handbook] "Medusa": candidate continuations form a
+ * tree scored in one pass; the longest accepted candidate prefix is kept.
+ *   t_j = argmax logits[b][j] (row j scores the children of node j);
+ *   node 0 (root) is accepted; node j >= 1 is accepted iff its parent is
+ *   accepted and token[b][j] == t_parent;
+ *   j* = the deepest accepted node, lowest id on ties;
+ *   accepted[b] = depth(j*); path[b] = node ids root -> j* (root excluded);
+ *   emitted[b] = token[path] ++ [t_{j*}]; both -1 padded.
+ *
+ *   logits [B][N][row_stride]; parent, token [B][N] int32 (parent[b][0] = -1,
+ *   parent[b][j] in [0, j); the root token is ignored)
+ *   accepted [B], path [B][N], emitted [B][N] int32 (out)
+ *   argmax_out [B][N] int32 or NULL (out), flags [B] or NULL (out)
+ * Limits: 1 <= B, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V <= SV_MAX_V.
+ */
+size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V);
+int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
+                   const int32_t *parent, const int32_t *token,
+                   int32_t B, int32_t N, int32_t V,
+                   int32_t *accepted, int32_t *path, int32_t *emitted,
+                   int32_t *argmax_out, uint32_t *flags,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_ngram_propose -- [Handbook] "N-gram" (take a suffix, find an earlier
+ * occurrence, copy what followed), [vLLM-03] "2. draft methods"
+ * (prompt_lookup_max down to prompt_lookup_min) and "3-1" (no match, no
+ * draft).  Per context b of length L = lengths[b]:
+ *   for n = n_max down to n_min: the most recent start s <= L-n-1 with
+ *   c[s .. s+n) == c[L-n .. L); the first n with a match wins;
+ *   proposal = c[s+n .. s+n+m), m = min(K, L-s-n);
+ *   no match: proposal_len 0, match_n 0, match_pos -1.
+ *
+ *   tokens [B][ctx_stride] int32, lengths [B] int32
+ *   proposal [B][K] int32 (out, -1 padded), proposal_len [B] int32 (out)
+ *   match_n, match_pos [B] int32 or NULL (out), flags [B] or NULL (out)
+ * Limits: 1 <= B, 1 <= n_min <= n_max <= SV_MAX_NGRAM,
+ *         0 <= K <= SV_MAX_PROPOSAL, 1 <= ctx_stride <= SV_MAX_CONTEXT.
+ * Needs no workspace.
+ */
+int sv_ngram_propose(const int32_t *tokens, int64_t ctx_stride,
+                     const int32_t *lengths, int32_t B,
+                     int32_t n_min, int32_t n_max, int32_t K,
+                     int32_t *proposal, int32_t *proposal_len,
+                     int32_t *match_n, int32_t *match_pos,
+                     uint32_t *flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,309 @@
+"""libspecverify: speculative-decoding verification and n-gram proposal on
+AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/specverify.h``.  It only
+marshals arguments: it allocates outputs (and a cached, zero-filled
+workspace) with torch on the tensors' device and passes raw device
+pointers and torch's current HIP stream.  Every step of the computation
+runs in the library's kernels.  If ``libspecverify.so`` has not been built
+the calls raise; there is no fallback path.
+
+    verify_greedy(logits, draft, draft_len=None)          -> dict
+    verify_rejection(target, draft_logits, draft, uniforms, temperature=1.0, draft_len=None)
+    verify_tree(logits, parent, token)
+    ngram_propose(tokens, lengths, n_min, n_max, K)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_F32, SV_BF16 = 0, 1
+FLAG_DRAFT_OOR, FLAG_BAD_LEN, FLAG_BAD_PARENT = 1, 2, 4
+TUNE_TARGET_WORKGROUPS, TUNE_MIN_SEGMENT_BYTES = 1, 2
+
+# every symbol include/specverify.h declares
+EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_set_tuning",
+           "sv_greedy_workspace_bytes", "sv_verify_greedy",
+           "sv_rejection_workspace_bytes", "sv_verify_rejection",
+           "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), message))
+        self.status = status
+
+
+_STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED", 3: "SV_ERR_WORKSPACE",
+           4: "SV_ERR_HIP"}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str = LIB_PATH):
+    """Load the shared library and declare its C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libspecverify.so is not built (%s); run "
+                               "proposal_sv_verify_amd.build.build() first" % path)
+        L = ctypes.CDLL(path)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.sv_abi_version.restype = ctypes.c_int
+        L.sv_abi_version.argtypes = []
+        L.sv_status_string.restype = ctypes.c_char_p
+        L.sv_status_string.argtypes = [ctypes.c_int]
+        L.sv_last_error_message.restype = ctypes.c_char_p
+        L.sv_last_error_message.argtypes = []
+        L.sv_set_tuning.restype = ctypes.c_int
+        L.sv_set_tuning.argtypes = [i32, i64]
+        for f in ("sv_greedy_workspace_bytes", "sv_rejection_workspace_bytes",
+                  "sv_tree_workspace_bytes"):
+            getattr(L, f).restype = sz
+            getattr(L, f).argtypes = [i32, i32, i32]
+        L.sv_verify_greedy.restype = ctypes.c_int
+        L.sv_verify_greedy.argtypes = [P, i32, i64, P, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
+        L.sv_verify_rejection.restype = ctypes.c_int
+        L.sv_verify_rejection.argtypes = [P, P, i32, i64, P, P, P, ctypes.c_float, i32, i32, i32,
+                                          P, P, P, P, P, P, P, sz, P]
+        L.sv_verify_tree.restype = ctypes.c_int
+        L.sv_verify_tree.argtypes = [P, i32, i64, P, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
+        L.sv_ngram_propose.restype = ctypes.c_int
+        L.sv_ngram_propose.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P, P, P]
+        _lib = L
+        return L
+
+
+def _check(status):
+    if status != SV_OK:
+        msg = load().sv_last_error_message().decode(errors="replace")
+        raise SpecVerifyError(status, msg)
+
+
+def set_tuning(key: int, value: int):
+    _check(load().sv_set_tuning(key, value))
+
+
+# ---------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device, stream=None):
+    """A zero-filled device buffer of at least nbytes, cached per (device,
+    stream): the kernels leave their counters at zero, so it is reused as is.
+    Calls on one stream are ordered, so sharing it there is safe."""
+    torch = _torch()
+    dev = torch.device(device)
+    key = (dev.index, stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _logits_args(x, name, rows_dims):
+    """Validate a [.., V] logits tensor whose leading dims are evenly spaced
+    rows; returns (dtype code, row stride in elements)."""
+    torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if x.dtype == torch.bfloat16:
+        code = SV_BF16
+    elif x.dtype == torch.float32:
+        code = SV_F32
+    else:
+        raise TypeError("%s must be float32 or bfloat16, got %s" % (name, x.dtype))
+    if x.dim() != rows_dims + 1 or x.stride(-1) != 1:
+        raise ValueError("%s must be [%s, V] with unit stride along V" % (name, "..." * rows_dims))
+    rs = x.stride(-2)
+    for d in range(rows_dims - 1):
+        if x.stride(d) != x.size(d + 1) * x.stride(d + 1):
+            raise ValueError("%s rows must be evenly spaced; call .contiguous()" % name)
+    return code, rs
+
+
+def _i32(t, shape, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be a contiguous int32 tensor of shape %s" % (name, tuple(shape)))
+    return t
+
+
+# ---------------------------------------------------------------- calls
+
+class Prepared:
+    """One library call with its arguments and output tensors bound.  Calling
+    it enqueues the kernels again on the stream it was prepared for and
+    returns the same output dict (overwritten in place)."""
+
+    def __init__(self, fn, args, out, keep):
+        self._fn = fn
+        self._args = args
+        self.out = out
+        # the raw pointers in args stay valid only while these tensors live
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
+def prepare_greedy(logits, draft, draft_len=None, *, want_argmax=True, stats=None):
+    """Greedy verification.  logits [B, K+1, V] (f32/bf16), draft [B, K]
+    int32, draft_len [B] int32 or None, stats int64 [3+K] or None
+    (accumulated in place).  Outputs: accepted [B], emitted [B, K+1],
+    argmax [B, K+1] (if want_argmax), flags [B]."""
+    torch = _torch()
+    L = load()
+    code, rs = _logits_args(logits, "logits", 2)
+    B, K1, V = logits.shape
+    K = K1 - 1
+    dev = logits.device
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 3 + K):
+        raise ValueError("stats must be an int64 tensor of at least 3+K entries")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, K1, dtype=torch.int32, device=dev)
+    amx = torch.empty(B, K1, dtype=torch.int32, device=dev) if want_argmax else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    s = _stream(dev)
+    ws = workspace(L.sv_greedy_workspace_bytes(B, K, V), dev, s)
+    args = (logits.data_ptr(), code, rs, _ptr(draft), _ptr(draft_len), B, K, V, acc.data_ptr(),
+            emi.data_ptr(), _ptr(amx), flg.data_ptr(), _ptr(stats), ws.data_ptr(), ws.numel(), s)
+    out = dict(accepted=acc, emitted=emi, flags=flg)
+    if want_argmax:
+        out["argmax"] = amx
+    return Prepared(L.sv_verify_greedy, args, out, (logits, draft, draft_len, stats, ws))
+
+
+def verify_greedy(*a, **k):
+    return prepare_greedy(*a, **k)()
+
+
+def prepare_rejection(target, draft_logits, draft, uniforms, temperature=1.0, draft_len=None, *,
+                      want_probs=True, stats=None):
+    """Rejection-sampling verification.  target [B, K+1, V], draft_logits
+    [B, K, V] (same dtype and row spacing), draft [B, K] int32, uniforms
+    [B, K+1] float32.  Outputs: accepted, emitted, p_draft, q_draft, flags."""
+    torch = _torch()
+    L = load()
+    code, rs = _logits_args(target, "target", 2)
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    if K > 0:
+        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2)
+        if code2 != code or rs2 != rs or tuple(draft_logits.shape) != (B, K, V):
+            raise ValueError("draft_logits must be [B, K, V] with the target's dtype and row stride")
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    if uniforms.dtype != torch.float32 or not uniforms.is_contiguous() or \
+            tuple(uniforms.shape) != (B, K1):
+        raise ValueError("uniforms must be a contiguous float32 tensor [B, K+1]")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 3 + K):
+        raise ValueError("stats must be an int64 tensor of at least 3+K entries")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, K1, dtype=torch.int32, device=dev)
+    pd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    qd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    s = _stream(dev)
+    ws = workspace(L.sv_rejection_workspace_bytes(B, K, V), dev, s)
+    args = (target.data_ptr(), _ptr(draft_logits) if K > 0 else None, code, rs, _ptr(draft),
+            _ptr(draft_len), uniforms.data_ptr(), float(temperature), B, K, V, acc.data_ptr(),
+            emi.data_ptr(), _ptr(pd), _ptr(qd), flg.data_ptr(), _ptr(stats), ws.data_ptr(),
+            ws.numel(), s)
+    out = dict(accepted=acc, emitted=emi, flags=flg)
+    if want_probs:
+        out["p_draft"], out["q_draft"] = pd, qd
+    return Prepared(L.sv_verify_rejection, args, out,
+                    (target, draft_logits, draft, draft_len, uniforms, stats, ws))
+
+
+def verify_rejection(*a, **k):
+    return prepare_rejection(*a, **k)()
+
+
+def prepare_tree(logits, parent, token, *, want_argmax=True):
+    """Tree verification.  logits [B, N, V], parent [B, N], token [B, N]
+    int32.  Outputs: accepted [B], path [B, N], emitted [B, N], argmax, flags."""
+    torch = _torch()
+    L = load()
+    code, rs = _logits_args(logits, "logits", 2)
+    B, N, V = logits.shape
+    dev = logits.device
+    _i32(parent, (B, N), "parent")
+    _i32(token, (B, N), "token")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, N, dtype=torch.int32, device=dev)
+    amx = torch.empty(B, N, dtype=torch.int32, device=dev) if want_argmax else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    s = _stream(dev)
+    ws = workspace(L.sv_tree_workspace_bytes(B, N, V), dev, s)
+    args = (logits.data_ptr(), code, rs, parent.data_ptr(), token.data_ptr(), B, N, V,
+            acc.data_ptr(), path.data_ptr(), emi.data_ptr(), _ptr(amx), flg.data_ptr(),
+            ws.data_ptr(), ws.numel(), s)
+    out = dict(accepted=acc, path=path, emitted=emi, flags=flg)
+    if want_argmax:
+        out["argmax"] = amx
+    return Prepared(L.sv_verify_tree, args, out, (logits, parent, token, ws))
+
+
+def verify_tree(*a, **k):
+    return prepare_tree(*a, **k)()
+
+
+def prepare_ngram(tokens, lengths, n_min, n_max, K):
+    """N-gram prompt lookup.  tokens [B, stride] int32 (unit inner stride),
+    lengths [B] int32.  Outputs: proposal [B, K], proposal_len [B],
+    match_n [B], match_pos [B], flags [B]."""
+    torch = _torch()
+    L = load()
+    if tokens.dtype != torch.int32 or tokens.dim() != 2 or tokens.stride(1) != 1:
+        raise ValueError("tokens must be an int32 [B, stride] tensor with unit inner stride")
+    B = tokens.shape[0]
+    stride = tokens.stride(0)
+    dev = tokens.device
+    _i32(lengths, (B,), "lengths")
+    prop = torch.empty(B, K, dtype=torch.int32, device=dev)
+    plen = torch.empty(B, dtype=torch.int32, device=dev)
+    mn = torch.empty(B, dtype=torch.int32, device=dev)
+    mp = torch.empty(B, dtype=torch.int32, device=dev)
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    args = (tokens.data_ptr(), stride, lengths.data_ptr(), B, n_min, n_max, K,
+            prop.data_ptr() if K > 0 else None, plen.data_ptr(), mn.data_ptr(), mp.data_ptr(),
+            flg.data_ptr(), _stream(dev))
+    out = dict(proposal=prop, proposal_len=plen, match_n=mn, match_pos=mp, flags=flg)
+    return Prepared(L.sv_ngram_propose, args, out, (tokens, lengths))
+
+
+def ngram_propose(*a, **k):
+    return prepare_ngram(*a, **k)()

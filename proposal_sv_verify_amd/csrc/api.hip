@@ -1,0 +1,508 @@
+// api.hip -- host side of libspecverify: argument validation, launch
+// planning, workspace layout and dispatch of the gfx950 kernels.  Every
+// check runs before anything is enqueued; a rejected call writes nothing.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "specverify.h"
+#include "sv_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- device check
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_arch_once[kMaxDevices];
+int g_arch_ok[kMaxDevices];
+
+int check_device()
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SV_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::call_once(g_arch_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        g_arch_ok[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                                 std::strncmp(prop.gcnArchName, "gfx950", 6) == 0
+                             ? 1
+                             : -1;
+    });
+    if (g_arch_ok[dev] != 1)
+        return fail(SV_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return SV_OK;
+}
+
+// ---------------------------------------------------------------- planning
+
+// Launch shape of a row-streaming kernel: every row is cut into `segs`
+// segments so that the grid holds about kTargetWorkgroups workgroups (8 per
+// CU on 256 CUs) without making segments smaller than kMinSegBytes.
+int64_t g_target_wgs = 2048;
+int64_t g_min_seg_bytes = 32 * 1024;
+
+struct RowPlan {
+    int segs;
+    int seg_len;
+};
+
+RowPlan plan_rows(int64_t rows, int V, int esize)
+{
+    int64_t segs = (g_target_wgs + rows - 1) / rows;
+    const int64_t by_size = (static_cast<int64_t>(V) * esize) / g_min_seg_bytes;
+    if (segs > by_size)
+        segs = by_size;
+    if (segs < 1)
+        segs = 1;
+    // segment length: a multiple of 64 elements so that segment starts keep
+    // the 16-byte alignment of the row
+    int64_t seg_len = (V + segs - 1) / segs;
+    seg_len = (seg_len + 63) / 64 * 64;
+    segs = (V + seg_len - 1) / seg_len;
+    return RowPlan{static_cast<int>(segs), static_cast<int>(seg_len)};
+}
+
+size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
+
+// Byte offsets of the workspace pieces of one call.
+struct ArgLayout {
+    size_t partial, row_ctr, seq_ctr, amax, total;
+};
+
+ArgLayout arg_layout(int64_t B, int64_t rows_per_seq, const RowPlan &pl)
+{
+    const int64_t rows = B * rows_per_seq;
+    ArgLayout L{};
+    size_t off = 0;
+    L.seq_ctr = off;
+    off = align_up(off + sizeof(unsigned) * B);
+    L.row_ctr = off;
+    off = align_up(off + (pl.segs > 1 ? sizeof(unsigned) * rows : 0));
+    L.partial = off;
+    off = align_up(off + (pl.segs > 1 ? sizeof(sv::ArgPartial) * rows * pl.segs : 0));
+    L.amax = off;
+    off = align_up(off + sizeof(int32_t) * rows);
+    L.total = off;
+    return L;
+}
+
+struct RejLayout {
+    size_t seq_ctr, chunk_ctr, row_ctr, partial, rstat, seq_n, cmass, total;
+};
+
+RejLayout rej_layout(int64_t B, int64_t K, int V, const RowPlan &pl)
+{
+    const int64_t rows = B * (2 * K + 1);
+    const int64_t nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
+    RejLayout L{};
+    size_t off = 0;
+    L.seq_ctr = off;
+    off = align_up(off + sizeof(unsigned) * B);
+    L.chunk_ctr = off;
+    off = align_up(off + sizeof(unsigned) * B);
+    L.row_ctr = off;
+    off = align_up(off + (pl.segs > 1 ? sizeof(unsigned) * rows : 0));
+    L.partial = off;
+    off = align_up(off + (pl.segs > 1 ? sizeof(sv::SoftPartial) * rows * pl.segs : 0));
+    L.rstat = off;
+    off = align_up(off + sizeof(sv::SoftPartial) * rows);
+    L.seq_n = off;
+    off = align_up(off + sizeof(int32_t) * B);
+    L.cmass = off;
+    off = align_up(off + sizeof(sv::ChunkMass) * B * nchunks);
+    L.total = off;
+    return L;
+}
+
+int esize_of(int dtype) { return dtype == SV_BF16 ? 2 : 4; }
+
+bool misaligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+template <typename T>
+T *at(void *base, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+int check_logits(const void *logits, int dtype, int64_t row_stride, int V, const char *name)
+{
+    if (dtype != SV_F32 && dtype != SV_BF16)
+        return fail(SV_ERR_INVALID_ARG, "dtype %d is neither SV_F32 nor SV_BF16", dtype);
+    if (!logits)
+        return fail(SV_ERR_INVALID_ARG, "%s is NULL", name);
+    if (misaligned(logits, esize_of(dtype)))
+        return fail(SV_ERR_INVALID_ARG, "%s is not aligned to its element size", name);
+    if (row_stride < V)
+        return fail(SV_ERR_INVALID_ARG, "row_stride %lld < V %d", (long long)row_stride, V);
+    return SV_OK;
+}
+
+int check_workspace(void *ws, size_t have, size_t need)
+{
+    if (!ws)
+        return fail(SV_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (misaligned(ws, 16))
+        return fail(SV_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    if (have < need)
+        return fail(SV_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    return SV_OK;
+}
+
+int check_sizes(int32_t B, int32_t K, int32_t V)
+{
+    if (B < 1)
+        return fail(SV_ERR_INVALID_ARG, "B = %d < 1", B);
+    if (K < 0)
+        return fail(SV_ERR_INVALID_ARG, "K = %d < 0", K);
+    if (V < 1)
+        return fail(SV_ERR_INVALID_ARG, "V = %d < 1", V);
+    if (K > SV_MAX_DRAFTS)
+        return fail(SV_ERR_UNSUPPORTED, "K = %d above %d", K, SV_MAX_DRAFTS);
+    if (V > SV_MAX_V)
+        return fail(SV_ERR_UNSUPPORTED, "V = %d above %d", V, SV_MAX_V);
+    return SV_OK;
+}
+
+int check_grid(int64_t wgs)
+{
+    if (wgs > 0x7fffffffLL)
+        return fail(SV_ERR_UNSUPPORTED, "launch of %lld workgroups is too large", (long long)wgs);
+    return SV_OK;
+}
+
+} // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char *sv_status_string(int status)
+{
+    switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_INVALID_ARG: return "SV_ERR_INVALID_ARG";
+    case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+    case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE";
+    case SV_ERR_HIP: return "SV_ERR_HIP";
+    default: return "SV_ERR_UNKNOWN";
+    }
+}
+
+const char *sv_last_error_message(void) { return g_err.c_str(); }
+
+int sv_set_tuning(int32_t key, int64_t value)
+{
+    if (key == SV_TUNE_TARGET_WORKGROUPS) {
+        g_target_wgs = value > 0 ? value : 2048;
+        return SV_OK;
+    }
+    if (key == SV_TUNE_MIN_SEGMENT_BYTES) {
+        g_min_seg_bytes = value > 0 ? value : 32 * 1024;
+        return SV_OK;
+    }
+    return fail(SV_ERR_INVALID_ARG, "unknown tuning key %d", key);
+}
+
+// ------------------------------------------------------------------ greedy
+
+size_t sv_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V)
+{
+    if (B < 1 || K < 0 || V < 1)
+        return 0;
+    const RowPlan a = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 2);
+    const RowPlan b = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 4);
+    const size_t x = arg_layout(B, K + 1, a).total, y = arg_layout(B, K + 1, b).total;
+    return x > y ? x : y;
+}
+
+int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
+                     const int32_t *draft, const int32_t *draft_len,
+                     int32_t B, int32_t K, int32_t V,
+                     int32_t *accepted, int32_t *emitted, int32_t *argmax_out,
+                     uint32_t *flags, int64_t *stats,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if ((st = check_sizes(B, K, V)) != SV_OK)
+        return st;
+    if ((st = check_logits(logits, dtype, row_stride, V, "logits")) != SV_OK)
+        return st;
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if (!accepted || !emitted)
+        return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
+    const int64_t rows = static_cast<int64_t>(B) * (K + 1);
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const ArgLayout L = arg_layout(B, K + 1, pl);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    if ((st = check_grid(rows * pl.segs)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::ArgVerifyParams p{};
+    p.logits = logits;
+    p.row_stride = row_stride;
+    p.B = B;
+    p.V = V;
+    p.rows_per_seq = K + 1;
+    p.segs = pl.segs;
+    p.seg_len = pl.seg_len;
+    p.draft = draft;
+    p.draft_len = draft_len;
+    p.K = K;
+    p.stats = stats;
+    p.accepted = accepted;
+    p.emitted = emitted;
+    p.amax = argmax_out ? argmax_out : at<int32_t>(workspace, L.amax);
+    p.amax_scratch = argmax_out ? 0 : 1;
+    p.flags = flags;
+    p.partial = at<sv::ArgPartial>(workspace, L.partial);
+    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
+    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
+    hipError_t e = sv::launch_greedy(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "greedy launch");
+    return SV_OK;
+}
+
+// ------------------------------------------------------------------ tree
+
+size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V)
+{
+    if (B < 1 || N < 1 || V < 1)
+        return 0;
+    const RowPlan a = plan_rows(static_cast<int64_t>(B) * N, V, 2);
+    const RowPlan b = plan_rows(static_cast<int64_t>(B) * N, V, 4);
+    const size_t x = arg_layout(B, N, a).total, y = arg_layout(B, N, b).total;
+    return x > y ? x : y;
+}
+
+int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
+                   const int32_t *parent, const int32_t *token,
+                   int32_t B, int32_t N, int32_t V,
+                   int32_t *accepted, int32_t *path, int32_t *emitted,
+                   int32_t *argmax_out, uint32_t *flags,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if (B < 1)
+        return fail(SV_ERR_INVALID_ARG, "B = %d < 1", B);
+    if (N < 1)
+        return fail(SV_ERR_INVALID_ARG, "N = %d < 1", N);
+    if (V < 1)
+        return fail(SV_ERR_INVALID_ARG, "V = %d < 1", V);
+    if (N > SV_MAX_TREE_NODES)
+        return fail(SV_ERR_UNSUPPORTED, "N = %d above %d", N, SV_MAX_TREE_NODES);
+    if (V > SV_MAX_V)
+        return fail(SV_ERR_UNSUPPORTED, "V = %d above %d", V, SV_MAX_V);
+    if ((st = check_logits(logits, dtype, row_stride, V, "logits")) != SV_OK)
+        return st;
+    if (!parent || !token)
+        return fail(SV_ERR_INVALID_ARG, "parent and token are required");
+    if (!accepted || !path || !emitted)
+        return fail(SV_ERR_INVALID_ARG, "accepted, path and emitted are required");
+    const int64_t rows = static_cast<int64_t>(B) * N;
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const ArgLayout L = arg_layout(B, N, pl);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    if ((st = check_grid(rows * pl.segs)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::ArgVerifyParams p{};
+    p.logits = logits;
+    p.row_stride = row_stride;
+    p.B = B;
+    p.V = V;
+    p.rows_per_seq = N;
+    p.segs = pl.segs;
+    p.seg_len = pl.seg_len;
+    p.parent = parent;
+    p.token = token;
+    p.path = path;
+    p.accepted = accepted;
+    p.emitted = emitted;
+    p.amax = argmax_out ? argmax_out : at<int32_t>(workspace, L.amax);
+    p.amax_scratch = argmax_out ? 0 : 1;
+    p.flags = flags;
+    p.partial = at<sv::ArgPartial>(workspace, L.partial);
+    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
+    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
+    hipError_t e = sv::launch_tree(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "tree launch");
+    return SV_OK;
+}
+
+// ------------------------------------------------------------------ rejection
+
+size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V)
+{
+    if (B < 1 || K < 0 || V < 1)
+        return 0;
+    const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
+    const RowPlan a = plan_rows(rows, V, 2);
+    const RowPlan b = plan_rows(rows, V, 4);
+    const size_t x = rej_layout(B, K, V, a).total, y = rej_layout(B, K, V, b).total;
+    return x > y ? x : y;
+}
+
+int sv_verify_rejection(const void *target_logits, const void *draft_logits,
+                        int32_t dtype, int64_t row_stride,
+                        const int32_t *draft, const int32_t *draft_len,
+                        const float *uniforms, float temperature,
+                        int32_t B, int32_t K, int32_t V,
+                        int32_t *accepted, int32_t *emitted,
+                        float *p_draft, float *q_draft,
+                        uint32_t *flags, int64_t *stats,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if ((st = check_sizes(B, K, V)) != SV_OK)
+        return st;
+    if ((st = check_logits(target_logits, dtype, row_stride, V, "target_logits")) != SV_OK)
+        return st;
+    if (K > 0 && (st = check_logits(draft_logits, dtype, row_stride, V, "draft_logits")) != SV_OK)
+        return st;
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if (!uniforms)
+        return fail(SV_ERR_INVALID_ARG, "uniforms is NULL");
+    if (!(std::isfinite(temperature) && temperature > 0.0f))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if (!accepted || !emitted)
+        return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
+    const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const RejLayout L = rej_layout(B, K, V, pl);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    const int nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
+    if ((st = check_grid(rows * pl.segs)) != SV_OK)
+        return st;
+    if ((st = check_grid(static_cast<int64_t>(B) * nchunks)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::RejectParams p{};
+    p.target = target_logits;
+    p.draftl = draft_logits;
+    p.row_stride = row_stride;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.segs = pl.segs;
+    p.seg_len = pl.seg_len;
+    p.nchunks = nchunks;
+    p.inv_t_d = 1.0 / static_cast<double>(temperature);
+    p.inv_t = static_cast<float>(p.inv_t_d);
+    p.draft = draft;
+    p.draft_len = draft_len;
+    p.u = uniforms;
+    p.accepted = accepted;
+    p.emitted = emitted;
+    p.p_draft = p_draft;
+    p.q_draft = q_draft;
+    p.flags = flags;
+    p.stats = stats;
+    p.partial = at<sv::SoftPartial>(workspace, L.partial);
+    p.rstat = at<sv::SoftPartial>(workspace, L.rstat);
+    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
+    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
+    p.seq_n = at<int32_t>(workspace, L.seq_n);
+    p.cmass = at<sv::ChunkMass>(workspace, L.cmass);
+    p.chunk_ctr = at<unsigned>(workspace, L.chunk_ctr);
+    hipError_t e = sv::launch_rejection(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "rejection launch");
+    return SV_OK;
+}
+
+// ------------------------------------------------------------------ n-gram
+
+int sv_ngram_propose(const int32_t *tokens, int64_t ctx_stride,
+                     const int32_t *lengths, int32_t B,
+                     int32_t n_min, int32_t n_max, int32_t K,
+                     int32_t *proposal, int32_t *proposal_len,
+                     int32_t *match_n, int32_t *match_pos,
+                     uint32_t *flags, void *stream)
+{
+    if (B < 1)
+        return fail(SV_ERR_INVALID_ARG, "B = %d < 1", B);
+    if (n_min < 1 || n_max < n_min)
+        return fail(SV_ERR_INVALID_ARG, "need 1 <= n_min <= n_max (got %d, %d)", n_min, n_max);
+    if (n_max > SV_MAX_NGRAM)
+        return fail(SV_ERR_UNSUPPORTED, "n_max = %d above %d", n_max, SV_MAX_NGRAM);
+    if (K < 0)
+        return fail(SV_ERR_INVALID_ARG, "K = %d < 0", K);
+    if (K > SV_MAX_PROPOSAL)
+        return fail(SV_ERR_UNSUPPORTED, "K = %d above %d", K, SV_MAX_PROPOSAL);
+    if (ctx_stride < 1)
+        return fail(SV_ERR_INVALID_ARG, "ctx_stride = %lld < 1", (long long)ctx_stride);
+    if (ctx_stride > SV_MAX_CONTEXT)
+        return fail(SV_ERR_UNSUPPORTED, "ctx_stride = %lld above %d", (long long)ctx_stride,
+                    SV_MAX_CONTEXT);
+    if (!tokens || !lengths)
+        return fail(SV_ERR_INVALID_ARG, "tokens and lengths are required");
+    if (misaligned(tokens, 4))
+        return fail(SV_ERR_INVALID_ARG, "tokens is not 4-byte aligned");
+    if (!proposal_len || (K > 0 && !proposal))
+        return fail(SV_ERR_INVALID_ARG, "proposal and proposal_len are required");
+    int st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+    sv::NgramParams p{};
+    p.tokens = tokens;
+    p.ctx_stride = ctx_stride;
+    p.lengths = lengths;
+    p.B = B;
+    p.n_min = n_min;
+    p.n_max = n_max;
+    p.K = K;
+    p.proposal = proposal;
+    p.proposal_len = proposal_len;
+    p.match_n = match_n;
+    p.match_pos = match_pos;
+    p.flags = flags;
+    p.vec_ok = !misaligned(tokens, 16) && (ctx_stride % 4 == 0);
+    hipError_t e = sv::launch_ngram(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "n-gram launch");
+    return SV_OK;
+}
+
+} // extern "C"

@@ -77,6 +77,8 @@ def _plant(rng, top: np.ndarray, V: int, alpha: float) -> np.ndarray:
     among the V-1 others (so every draft is accepted with probability alpha
     exactly, independently per position)."""
     hit = rng.random(top.shape) < alpha
+    if V == 1:                      # no other id exists: every draft is the argmax
+        return np.asarray(top, np.int32).copy()
     other = rng.integers(0, V - 1, size=top.shape)
     other = other + (other >= top)
     return np.where(hit, top, other).astype(np.int32)

@@ -1,0 +1,154 @@
+"""The C ABI library: it loads, exports every symbol the header declares, and
+rejects invalid arguments on the host before any HIP call (no GPU needed:
+none of these calls reaches a kernel launch or a device query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import proposal_sv_verify_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIB_PATH):
+        from proposal_sv_verify_amd import build
+        build.build()
+    return sv.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(sv.EXPORTS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", sv.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert getattr(lib, f) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sv_abi_version() == 1
+    assert lib.sv_status_string(0) == b"SV_OK"
+    assert lib.sv_status_string(3) == b"SV_ERR_WORKSPACE"
+    assert lib.sv_status_string(99) == b"SV_ERR_UNKNOWN"
+
+
+FAKE = 0x10000          # a 64 KiB-aligned non-null address, never dereferenced
+BIG = 1 << 40
+
+
+def _greedy(lib, **kw):
+    a = dict(logits=FAKE, dtype=1, row_stride=100, draft=FAKE, draft_len=None, B=2, K=3, V=100,
+             acc=FAKE, emi=FAKE, amx=None, flags=None, stats=None, ws=FAKE, wsb=BIG, stream=None)
+    a.update(kw)
+    return lib.sv_verify_greedy(a["logits"], a["dtype"], a["row_stride"], a["draft"],
+                                a["draft_len"], a["B"], a["K"], a["V"], a["acc"], a["emi"],
+                                a["amx"], a["flags"], a["stats"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=-1), sv.SV_ERR_INVALID_ARG),
+    (dict(V=0), sv.SV_ERR_INVALID_ARG),
+    (dict(K=5000), sv.SV_ERR_UNSUPPORTED),
+    (dict(dtype=7), sv.SV_ERR_INVALID_ARG),
+    (dict(logits=None), sv.SV_ERR_INVALID_ARG),
+    (dict(logits=FAKE + 1), sv.SV_ERR_INVALID_ARG),     # bf16 needs 2-byte alignment
+    (dict(row_stride=99), sv.SV_ERR_INVALID_ARG),
+    (dict(draft=None), sv.SV_ERR_INVALID_ARG),
+    (dict(acc=None), sv.SV_ERR_INVALID_ARG),
+    (dict(ws=None), sv.SV_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), sv.SV_ERR_WORKSPACE),
+    (dict(wsb=16), sv.SV_ERR_WORKSPACE),
+])
+def test_greedy_rejects_bad_arguments(lib, kw, status):
+    assert _greedy(lib, **kw) == status
+    assert lib.sv_last_error_message()
+
+
+def test_workspace_sizes(lib):
+    assert lib.sv_greedy_workspace_bytes(0, 3, 10) == 0
+    g = lib.sv_greedy_workspace_bytes(256, 8, 151936)
+    assert g >= 4 * 256 * 9 and g % 256 == 0
+    assert lib.sv_rejection_workspace_bytes(64, 5, 128256) > 0
+    assert lib.sv_tree_workspace_bytes(32, 64, 128256) > 0
+    # more rows than workgroups wanted -> one segment per row
+    assert lib.sv_set_tuning(1, 64) == 0
+    small = lib.sv_greedy_workspace_bytes(256, 8, 151936)
+    assert lib.sv_set_tuning(1, 0) == 0
+    assert small <= g
+    assert lib.sv_set_tuning(42, 1) == sv.SV_ERR_INVALID_ARG
+
+
+def test_rejection_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, rs=100, draft=FAKE, dl=None, u=FAKE, T=1.0, B=2, K=3,
+                 V=100, acc=FAKE, emi=FAKE, pd=None, qd=None, fl=None, st=None, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_verify_rejection(a["t"], a["d"], a["dtype"], a["rs"], a["draft"], a["dl"],
+                                       a["u"], a["T"], a["B"], a["K"], a["V"], a["acc"], a["emi"],
+                                       a["pd"], a["qd"], a["fl"], a["st"], a["ws"], a["wsb"], None)
+    assert call(T=0.0) == sv.SV_ERR_INVALID_ARG
+    assert call(T=float("nan")) == sv.SV_ERR_INVALID_ARG
+    assert call(T=float("inf")) == sv.SV_ERR_INVALID_ARG
+    assert call(T=-1.0) == sv.SV_ERR_INVALID_ARG
+    assert call(u=None) == sv.SV_ERR_INVALID_ARG
+    assert call(d=None) == sv.SV_ERR_INVALID_ARG
+    assert call(wsb=0) == sv.SV_ERR_WORKSPACE
+    assert call(emi=None) == sv.SV_ERR_INVALID_ARG
+
+
+def test_tree_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(l=FAKE, dtype=0, rs=100, par=FAKE, tok=FAKE, B=2, N=8, V=100, acc=FAKE,
+                 path=FAKE, emi=FAKE, amx=None, fl=None, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_verify_tree(a["l"], a["dtype"], a["rs"], a["par"], a["tok"], a["B"], a["N"],
+                                  a["V"], a["acc"], a["path"], a["emi"], a["amx"], a["fl"],
+                                  a["ws"], a["wsb"], None)
+    assert call(N=0) == sv.SV_ERR_INVALID_ARG
+    assert call(N=2000) == sv.SV_ERR_UNSUPPORTED
+    assert call(par=None) == sv.SV_ERR_INVALID_ARG
+    assert call(path=None) == sv.SV_ERR_INVALID_ARG
+    assert call(l=FAKE + 2) == sv.SV_ERR_INVALID_ARG       # fp32 needs 4-byte alignment
+    assert call(wsb=1) == sv.SV_ERR_WORKSPACE
+
+
+def test_ngram_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(tok=FAKE, stride=100, lens=FAKE, B=2, nmin=2, nmax=5, K=8, prop=FAKE,
+                 plen=FAKE)
+        a.update(kw)
+        return lib.sv_ngram_propose(a["tok"], a["stride"], a["lens"], a["B"], a["nmin"],
+                                    a["nmax"], a["K"], a["prop"], a["plen"], None, None, None,
+                                    None)
+    assert call(nmin=0) == sv.SV_ERR_INVALID_ARG
+    assert call(nmin=6) == sv.SV_ERR_INVALID_ARG
+    assert call(nmax=40) == sv.SV_ERR_UNSUPPORTED
+    assert call(K=-1) == sv.SV_ERR_INVALID_ARG
+    assert call(K=5000) == sv.SV_ERR_UNSUPPORTED
+    assert call(stride=0) == sv.SV_ERR_INVALID_ARG
+    assert call(stride=1 << 27) == sv.SV_ERR_UNSUPPORTED
+    assert call(tok=FAKE + 2) == sv.SV_ERR_INVALID_ARG
+    assert call(lens=None) == sv.SV_ERR_INVALID_ARG
+    assert call(prop=None) == sv.SV_ERR_INVALID_ARG
+    assert call(B=0) == sv.SV_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(sv, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        sv.load(str(tmp_path / "nope.so"))
