@@ -31,7 +31,9 @@
  *    frees nothing inside these calls.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call only enqueues kernels and returns; outputs are valid after
- *    the stream reaches that point.  No call synchronises.
+ *    the stream reaches that point.  No call synchronises, and no kernel
+ *    waits on another workgroup: each call is a short chain of kernels whose
+ *    boundaries order its phases.
  *  - Logits are fp32 (SV_F32) or bf16 (SV_BF16, raw IEEE bf16 bits) with
  *    `row_stride` elements between consecutive rows (row_stride >= V); the
  *    base pointer must be aligned to the element size.
@@ -40,13 +42,11 @@
  *    and sv_last_error_message() explains.  Malformed DATA found on the
  *    device has a defined result and sets a bit in flags[b] (flags may be
  *    NULL): see SV_FLAG_*.
- *  - Workspaces hold per-row partial results and arrival counters.  Size
- *    one with the matching sv_*_workspace_bytes(); it must be 16-byte
- *    aligned and ZERO-FILLED before its first use (hipMemset / torch.zeros).
- *    Every completed call leaves the whole workspace all-zero again, so one
- *    workspace serves any sequence of calls of any kind and size without
- *    clearing.  Calls that share a workspace must be ordered on one stream;
- *    calls running concurrently need their own.
+ *  - Workspaces are device scratch for per-row partial results; size one
+ *    with the matching sv_*_workspace_bytes() (16-byte aligned).  They need
+ *    no initialisation and their contents are undefined after a call.
+ *    Calls that share a workspace must be ordered on one stream; calls
+ *    running concurrently need their own.
  *  - argmax ties resolve to the LOWEST token id (the numpy / torch rule);
  *    -0.0 and +0.0 compare equal.  Rows must be free of NaN.
  *  - The device must be gfx950 (else SV_ERR_UNSUPPORTED).

@@ -2,7 +2,7 @@
 AMD Instinct MI355X (gfx950).
 
 Thin ctypes binding over the C ABI in ``include/specverify.h``.  It only
-marshals arguments: it allocates outputs (and a cached, zero-filled
+marshals arguments: it allocates outputs (and a cached scratch
 workspace) with torch on the tensors' device and passes raw device
 pointers and torch's current HIP stream.  Every step of the computation
 runs in the library's kernels.  If ``libspecverify.so`` has not been built
@@ -112,15 +112,14 @@ _ws_cache = {}
 
 
 def workspace(nbytes: int, device, stream=None):
-    """A zero-filled device buffer of at least nbytes, cached per (device,
-    stream): the kernels leave their counters at zero, so it is reused as is.
-    Calls on one stream are ordered, so sharing it there is safe."""
+    """A device scratch buffer of at least nbytes, cached per (device,
+    stream).  Calls on one stream are ordered, so sharing it there is safe."""
     torch = _torch()
     dev = torch.device(device)
     key = (dev.index, stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 

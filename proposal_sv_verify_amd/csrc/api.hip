@@ -93,28 +93,19 @@ size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 
 // Byte offsets of the workspace pieces of one call.
 struct ArgLayout {
-    size_t partial, row_ctr, seq_ctr, amax, total;
+    size_t partial, total;
 };
 
 ArgLayout arg_layout(int64_t B, int64_t rows_per_seq, const RowPlan &pl)
 {
-    const int64_t rows = B * rows_per_seq;
     ArgLayout L{};
-    size_t off = 0;
-    L.seq_ctr = off;
-    off = align_up(off + sizeof(unsigned) * B);
-    L.row_ctr = off;
-    off = align_up(off + (pl.segs > 1 ? sizeof(unsigned) * rows : 0));
-    L.partial = off;
-    off = align_up(off + (pl.segs > 1 ? sizeof(sv::ArgPartial) * rows * pl.segs : 0));
-    L.amax = off;
-    off = align_up(off + sizeof(int32_t) * rows);
-    L.total = off;
+    L.partial = 0;
+    L.total = align_up(sizeof(sv::ArgPartial) * B * rows_per_seq * pl.segs);
     return L;
 }
 
 struct RejLayout {
-    size_t seq_ctr, chunk_ctr, row_ctr, partial, rstat, seq_n, cmass, total;
+    size_t partial, seq, cmass, total;
 };
 
 RejLayout rej_layout(int64_t B, int64_t K, int V, const RowPlan &pl)
@@ -123,18 +114,10 @@ RejLayout rej_layout(int64_t B, int64_t K, int V, const RowPlan &pl)
     const int64_t nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
     RejLayout L{};
     size_t off = 0;
-    L.seq_ctr = off;
-    off = align_up(off + sizeof(unsigned) * B);
-    L.chunk_ctr = off;
-    off = align_up(off + sizeof(unsigned) * B);
-    L.row_ctr = off;
-    off = align_up(off + (pl.segs > 1 ? sizeof(unsigned) * rows : 0));
     L.partial = off;
-    off = align_up(off + (pl.segs > 1 ? sizeof(sv::SoftPartial) * rows * pl.segs : 0));
-    L.rstat = off;
-    off = align_up(off + sizeof(sv::SoftPartial) * rows);
-    L.seq_n = off;
-    off = align_up(off + sizeof(int32_t) * B);
+    off = align_up(off + sizeof(sv::SoftPartial) * rows * pl.segs);
+    L.seq = off;
+    off = align_up(off + sizeof(sv::SeqState) * B);
     L.cmass = off;
     off = align_up(off + sizeof(sv::ChunkMass) * B * nchunks);
     L.total = off;
@@ -284,12 +267,9 @@ int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
     p.stats = stats;
     p.accepted = accepted;
     p.emitted = emitted;
-    p.amax = argmax_out ? argmax_out : at<int32_t>(workspace, L.amax);
-    p.amax_scratch = argmax_out ? 0 : 1;
+    p.argmax_out = argmax_out;
     p.flags = flags;
     p.partial = at<sv::ArgPartial>(workspace, L.partial);
-    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
-    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
     hipError_t e = sv::launch_greedy(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "greedy launch");
@@ -355,12 +335,9 @@ int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
     p.path = path;
     p.accepted = accepted;
     p.emitted = emitted;
-    p.amax = argmax_out ? argmax_out : at<int32_t>(workspace, L.amax);
-    p.amax_scratch = argmax_out ? 0 : 1;
+    p.argmax_out = argmax_out;
     p.flags = flags;
     p.partial = at<sv::ArgPartial>(workspace, L.partial);
-    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
-    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
     hipError_t e = sv::launch_tree(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "tree launch");
@@ -440,12 +417,8 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     p.flags = flags;
     p.stats = stats;
     p.partial = at<sv::SoftPartial>(workspace, L.partial);
-    p.rstat = at<sv::SoftPartial>(workspace, L.rstat);
-    p.row_ctr = at<unsigned>(workspace, L.row_ctr);
-    p.seq_ctr = at<unsigned>(workspace, L.seq_ctr);
-    p.seq_n = at<int32_t>(workspace, L.seq_n);
+    p.seq = at<sv::SeqState>(workspace, L.seq);
     p.cmass = at<sv::ChunkMass>(workspace, L.cmass);
-    p.chunk_ctr = at<unsigned>(workspace, L.chunk_ctr);
     hipError_t e = sv::launch_rejection(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "rejection launch");

@@ -1,24 +1,23 @@
 // argmax_verify.hip -- greedy and tree verification on gfx950.
 //
-// One workgroup per (row, segment) streams its slice of the logits with
-// 16-byte loads and reduces a (value, index) argmax with the total order
-// "larger value, then lower token id".  When a row is cut into several
-// segments, the last segment to finish (arrival counter) merges them.  The
-// last row of a sequence to finish runs the per-sequence step:
+// Kernel 1 streams the logits: one workgroup per (row, segment) reads its
+// slice with 16-byte non-temporal loads and reduces a (value, index) argmax
+// with the total order "larger value, then lower token id", writing one
+// partial per segment.  Kernel 2 works per sequence: it merges the segment
+// partials of each row and runs
 //
 //  greedy  ([Arctic] "inference pipeline optimisation"; [Handbook] "how it
-//          works"; [vLLM-03] "1. principle"): accept the longest prefix of
-//          drafts equal to the row argmaxes, then emit the argmax of the
-//          first disagreeing (or last) row;
-//  tree    ([Handbook] "Medusa"): accept node j when its parent is accepted
-//          and its token equals the parent row's argmax; keep the deepest
-//          accepted node (lowest id on ties), emit the path and the argmax
-//          of the chosen node.
+//          works"; [vLLM-03] "1. principle"): one wave per sequence, one
+//          lane per draft position; a ballot of the positions whose draft
+//          differs from the row argmax gives the first disagreement n, and
+//          the wave writes drafts 0..n-1 plus the argmax of row n;
+//  tree    ([Handbook] "Medusa"): node j is accepted when its parent is
+//          accepted and its token equals the parent row's argmax; the
+//          deepest accepted node (lowest id on ties) gives the path and the
+//          bonus token.
 //
-// No kernel waits on another workgroup: arrival counters only elect the
-// workgroup that finishes a row or a sequence.  That workgroup resets the
-// counter and clears every workspace slot it consumed, so the workspace is
-// all-zero again when the kernel ends, whatever call used it before.
+// The kernel boundary orders the two phases: no workgroup ever waits for, or
+// fences against, another one.
 
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
@@ -26,21 +25,135 @@
 namespace sv {
 namespace {
 
-enum { kGreedy = 0, kTree = 1 };
-
-// Sequential tree scan of one sequence, run by thread 0 of the finishing
-// workgroup.  Shared arrays hold the row argmaxes, the chosen path and the
-// per-node depth / acceptance.
-__device__ void tree_finalize(const ArgVerifyParams &p, int b, int *s_t, int *s_depth,
-                              unsigned char *s_acc, int *s_path, int &s_best, int &s_bestd)
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_row_argmax(const ArgVerifyParams p)
 {
+    const int wg = blockIdx.x;
+    const int row = wg / p.segs;
+    const int seg = wg - row * p.segs;
+    // greedy rows past the draft length are never read
+    bool needed = true;
+    if (p.draft_len != nullptr) {
+        const int b = row / p.rows_per_seq;
+        unsigned unused = 0;
+        needed = row - b * p.rows_per_seq <= clamp_len(p.draft_len[b], p.K, unused);
+    }
+    float bv = -__builtin_inff();
+    int bi = kIdxNone;
+    if (needed) {
+        const E *rp = static_cast<const E *>(p.logits) + static_cast<int64_t>(row) * p.row_stride;
+        const int lo = seg * p.seg_len;
+        const int hi = min(p.V, lo + p.seg_len);
+        for_each_in_segment<E, 4>(
+            rp, lo, hi,
+            [&](const float(&f)[Elem<E>::kPerVec], int base) { arg_visit_vec(bv, bi, f, base); },
+            [&](float x, int idx) {
+                if (x > bv) {
+                    bv = x;
+                    bi = idx;
+                }
+            });
+    }
+    block_argmax(bv, bi);
+    if (threadIdx.x == 0)
+        p.partial[static_cast<int64_t>(row) * p.segs + seg] = ArgPartial{bv, bi};
+}
+
+// Row argmax from its segment partials.  A row whose elements all compare
+// false against -inf keeps the sentinel; id 0 is then the lowest id holding
+// the maximum.
+__device__ __forceinline__ int merged_argmax(const ArgVerifyParams &p, int64_t row)
+{
+    const ArgPartial *pp = p.partial + row * p.segs;
+    float bv = -__builtin_inff();
+    int bi = kIdxNone;
+    for (int s = 0; s < p.segs; ++s) {
+        const ArgPartial q = pp[s];
+        arg_combine(bv, bi, q.v, q.i);
+    }
+    return bi == kIdxNone ? 0 : bi;
+}
+
+// One wave per sequence, one lane per position (in blocks of 64 positions).
+__global__ __launch_bounds__(kThreads) void k_greedy_scan(const ArgVerifyParams p)
+{
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (b >= p.B)
+        return;
+    const int K = p.K;
+    unsigned fl = 0;
+    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, fl) : K;
+    const int *d = p.draft + static_cast<int64_t>(b) * K;
+    int *e = p.emitted + static_cast<int64_t>(b) * (K + 1);
+    int n = -1;          // wave-uniform once known
+    bool oor = false;
+    for (int base = 0; base <= K; base += 64) {
+        const int i = base + lane;
+        int t = -1;
+        if (i <= len)
+            t = merged_argmax(p, static_cast<int64_t>(b) * (K + 1) + i);
+        if (p.argmax_out && i <= K)
+            p.argmax_out[static_cast<int64_t>(b) * (K + 1) + i] = t;
+        const int x = i < len ? d[i] : 0;
+        if (i < len && (x < 0 || x >= p.V))
+            oor = true;
+        const unsigned long long mism = __ballot(i < len && x != t);
+        int here = -1;
+        if (n < 0) {
+            if (mism)
+                here = base + __builtin_ctzll(mism);
+            else if (len < base + 64)
+                here = len;          // every draft agreed: the bonus row is len
+        }
+        if (i <= K) {
+            int v;
+            if (n >= 0)
+                v = -1;              // decided in an earlier block
+            else if (here < 0)
+                v = x;               // no disagreement up to the end of this block
+            else
+                v = i < here ? x : (i == here ? t : -1);
+            e[i] = v;
+        }
+        if (n < 0)
+            n = here;
+    }
+    if (__ballot(oor))
+        fl |= SV_FLAG_DRAFT_OOR;
+    if (lane == 0) {
+        p.accepted[b] = n;
+        if (p.flags)
+            p.flags[b] = fl;
+        if (p.stats) {
+            stats_add(p.stats + 0, n);
+            stats_add(p.stats + 1, len);
+            stats_add(p.stats + 2, n + 1);
+        }
+    }
+    if (p.stats)
+        for (int i = lane; i < n; i += 64)
+            stats_add(p.stats + 3 + i, 1);
+}
+
+// One workgroup per tree; thread 0 walks the nodes in id order (parents
+// precede children), the workgroup writes the outputs.
+__global__ __launch_bounds__(kThreads) void k_tree_scan(const ArgVerifyParams p)
+{
+    __shared__ int s_t[SV_MAX_TREE_NODES];
+    __shared__ int s_depth[SV_MAX_TREE_NODES];
+    __shared__ int s_path[SV_MAX_TREE_NODES];
+    __shared__ unsigned char s_acc[SV_MAX_TREE_NODES];
+    __shared__ int s_best, s_bestd;
+    const int b = blockIdx.x;
     const int N = p.rows_per_seq;
     const int *par = p.parent + static_cast<int64_t>(b) * N;
     const int *tok = p.token + static_cast<int64_t>(b) * N;
     for (int j = threadIdx.x; j < N; j += kThreads) {
-        s_t[j] = p.amax[static_cast<int64_t>(b) * N + j];
-        if (p.amax_scratch)                  // the workspace is left all-zero
-            p.amax[static_cast<int64_t>(b) * N + j] = 0;
+        const int t = merged_argmax(p, static_cast<int64_t>(b) * N + j);
+        s_t[j] = t;
+        if (p.argmax_out)
+            p.argmax_out[static_cast<int64_t>(b) * N + j] = t;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -62,17 +175,17 @@ __device__ void tree_finalize(const ArgVerifyParams &p, int b, int *s_t, int *s_
                 continue;
             }
             const unsigned char a = s_acc[pj] && tj == s_t[pj];
-            const int d = s_depth[pj] + 1;
+            const int dj = s_depth[pj] + 1;
             s_acc[j] = a;
-            s_depth[j] = d;
-            if (a && d > bestd) {
-                bestd = d;
+            s_depth[j] = dj;
+            if (a && dj > bestd) {
+                bestd = dj;
                 best = j;
             }
         }
         int cur = best;
-        for (int d = bestd - 1; d >= 0; --d) {
-            s_path[d] = cur;
+        for (int dd = bestd - 1; dd >= 0; --dd) {
+            s_path[dd] = cur;
             cur = par[cur];
         }
         s_best = best;
@@ -90,135 +203,15 @@ __device__ void tree_finalize(const ArgVerifyParams &p, int b, int *s_t, int *s_
     }
 }
 
-// Greedy prefix scan of one sequence, run by thread 0 of the finishing
-// workgroup.
-__device__ void greedy_finalize(const ArgVerifyParams &p, int b)
-{
-    const int K = p.K;
-    unsigned fl = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, fl) : K;
-    const int *d = p.draft + static_cast<int64_t>(b) * K;
-    const int *t = p.amax + static_cast<int64_t>(b) * (K + 1);
-    int n = 0;
-    bool agree = true;
-    for (int i = 0; i < len; ++i) {
-        const int x = d[i];
-        if (x < 0 || x >= p.V)
-            fl |= SV_FLAG_DRAFT_OOR;
-        if (agree && x == t[i])
-            ++n;
-        else
-            agree = false;
-    }
-    int *e = p.emitted + static_cast<int64_t>(b) * (K + 1);
-    for (int i = 0; i <= K; ++i)
-        e[i] = i < n ? d[i] : (i == n ? t[n] : -1);
-    if (p.amax_scratch)                      // the workspace is left all-zero
-        for (int i = 0; i <= K; ++i)
-            p.amax[static_cast<int64_t>(b) * (K + 1) + i] = 0;
-    p.accepted[b] = n;
-    if (p.flags)
-        p.flags[b] = fl;
-    if (p.stats) {
-        stats_add(p.stats + 0, n);
-        stats_add(p.stats + 1, len);
-        stats_add(p.stats + 2, n + 1);
-        for (int i = 0; i < n; ++i)
-            stats_add(p.stats + 3 + i, 1);
-    }
-}
-
-template <typename E, int MODE>
-__global__ __launch_bounds__(kThreads) void k_argmax_verify(const ArgVerifyParams p)
-{
-    const int wg = blockIdx.x;
-    const int row = wg / p.segs;
-    const int seg = wg - row * p.segs;
-    const int b = row / p.rows_per_seq;
-    const int i = row - b * p.rows_per_seq;
-
-    // greedy rows past the draft length are not needed
-    bool needed = true;
-    if (MODE == kGreedy && p.draft_len != nullptr) {
-        unsigned unused = 0;
-        needed = i <= clamp_len(p.draft_len[b], p.K, unused);
-    }
-
-    float bv = -__builtin_inff();
-    int bi = kIdxNone;
-    if (needed) {
-        const E *rp = static_cast<const E *>(p.logits) + static_cast<int64_t>(row) * p.row_stride;
-        const int lo = seg * p.seg_len;
-        const int hi = min(p.V, lo + p.seg_len);
-        for_each_in_segment<E, 4>(
-            rp, lo, hi,
-            [&](const float(&f)[Elem<E>::kPerVec], int base) { arg_visit_vec(bv, bi, f, base); },
-            [&](float x, int idx) {
-                if (x > bv) {
-                    bv = x;
-                    bi = idx;
-                }
-            });
-    }
-    block_argmax(bv, bi);
-
-    __shared__ int s_last_row, s_last_seq;
-    if (p.segs > 1) {
-        if (threadIdx.x == 0) {
-            p.partial[static_cast<int64_t>(row) * p.segs + seg] = ArgPartial{bv, bi};
-            s_last_row = arrive(p.row_ctr + row) == static_cast<unsigned>(p.segs - 1);
-        }
-        __syncthreads();
-        if (!s_last_row)
-            return;
-        if (threadIdx.x == 0) {
-            reset_counter(p.row_ctr + row);
-            bv = -__builtin_inff();
-            bi = kIdxNone;
-            ArgPartial *pp = p.partial + static_cast<int64_t>(row) * p.segs;
-            for (int s = 0; s < p.segs; ++s) {
-                const ArgPartial q = pp[s];
-                arg_combine(bv, bi, q.v, q.i);
-                pp[s] = ArgPartial{0.0f, 0};    // the workspace is left all-zero
-            }
-        }
-    }
-    if (threadIdx.x == 0) {
-        // all elements equal to -inf (or NaN) leave the sentinel: id 0 is then
-        // the lowest id holding the maximum
-        p.amax[row] = needed ? (bi == kIdxNone ? 0 : bi) : -1;
-        s_last_seq = arrive(p.seq_ctr + b) == static_cast<unsigned>(p.rows_per_seq - 1);
-    }
-    __syncthreads();
-    if (!s_last_seq)
-        return;
-    acquire_agent();
-    if (threadIdx.x == 0)
-        reset_counter(p.seq_ctr + b);
-
-    if constexpr (MODE == kGreedy) {
-        if (threadIdx.x == 0)
-            greedy_finalize(p, b);
-    } else {
-        __shared__ int s_t[SV_MAX_TREE_NODES];
-        __shared__ int s_depth[SV_MAX_TREE_NODES];
-        __shared__ int s_path[SV_MAX_TREE_NODES];
-        __shared__ unsigned char s_acc[SV_MAX_TREE_NODES];
-        __shared__ int s_best, s_bestd;
-        tree_finalize(p, b, s_t, s_depth, s_acc, s_path, s_best, s_bestd);
-    }
-}
-
-template <int MODE>
-hipError_t launch_argmax(const ArgVerifyParams &p, int dtype, hipStream_t s)
+hipError_t launch_rows(const ArgVerifyParams &p, int dtype, hipStream_t s)
 {
     const int64_t grid = static_cast<int64_t>(p.B) * p.rows_per_seq * p.segs;
     if (dtype == SV_BF16)
-        hipLaunchKernelGGL((k_argmax_verify<uint16_t, MODE>), dim3(static_cast<unsigned>(grid)),
-                           dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(k_row_argmax<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                           0, s, p);
     else
-        hipLaunchKernelGGL((k_argmax_verify<float, MODE>), dim3(static_cast<unsigned>(grid)),
-                           dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(k_row_argmax<float>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                           s, p);
     return hipGetLastError();
 }
 
@@ -226,12 +219,23 @@ hipError_t launch_argmax(const ArgVerifyParams &p, int dtype, hipStream_t s)
 
 hipError_t launch_greedy(const ArgVerifyParams &p, int dtype, hipStream_t s)
 {
-    return launch_argmax<kGreedy>(p, dtype, s);
+    hipError_t e = launch_rows(p, dtype, s);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_greedy_scan, dim3(static_cast<unsigned>((p.B + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, s, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_tree(const ArgVerifyParams &p, int dtype, hipStream_t s)
 {
-    return launch_argmax<kTree>(p, dtype, s);
+    ArgVerifyParams q = p;
+    q.draft_len = nullptr;          // every node row is needed
+    hipError_t e = launch_rows(q, dtype, s);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_tree_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, q);
+    return hipGetLastError();
 }
 
 } // namespace sv

@@ -2,27 +2,27 @@
 // al. / Chen et al., the rule [vLLM-03] "1. principle" cites for keeping the
 // target distribution at T > 0).
 //
-// Kernel 1 (row statistics + accept scan).  One workgroup per (row,
-// segment) over the K+1 target rows and K draft rows of every sequence
-// streams the logits once with 16-byte loads and keeps, per thread, an
-// online (max, sum of exp) pair: the max is taken per 8-element vector, the
-// exp is fp32 (expf) relative to the running max, sums are fp64, and a new
-// max rescales the fp64 sum with an fp64 exp.  Segments merge through an
-// arrival counter; the last row of a sequence runs the accept scan:
-// p_i(x_i) and q_i(x_i) with fp64 exp from the row max and normaliser, the
-// test u_i < p/q in fp64, and the first rejection n.
+// Kernel 1 (row statistics).  One workgroup per (row, segment) over the
+// K+1 target rows and K draft rows of every sequence streams the logits
+// once with 16-byte loads and keeps, per thread, an online (max, sum of exp)
+// pair: the max is taken per 8-element vector, the exp is fp32 (expf)
+// relative to the running max, sums are fp64, and a new max rescales the
+// fp64 sum with an fp64 exp.  Each segment writes (max, sum).
 //
-// Kernel 2 (final sample).  The final token is drawn from one row pair per
-// sequence: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
-// zero), or p_n when every draft was accepted.  B x C workgroups each take a
-// chunk of the row pair, form r per element (fp32 exp, fp64 after), and
-// publish the chunk's mass; the last chunk of a sequence finds the chunk
-// where the running mass first exceeds u_K * S and scans it in token order
-// for the token whose cumulative mass first exceeds it.
+// Kernel 2 (accept scan + final-sample masses).  One workgroup per
+// (sequence, chunk).  Wave 0 merges the segment statistics of the rows it
+// needs, computes p_i(x_i) and q_i(x_i) with fp64 exp, tests u_i < p/q in
+// fp64 and finds the first rejection n.  The final token is drawn from one
+// row pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
+// zero), or p_n when every draft was accepted.  Each workgroup forms r
+// over its chunk of the row pair (fp32 exp, fp64 after) and writes the
+// chunk's masses.
 //
-// Arrival counters only elect the workgroup that finishes a row, a sequence
-// or a sequence's chunks; it resets the counter and clears the workspace
-// slots it consumed, so the workspace is all-zero again after the call.
+// Kernel 3 (selection).  One workgroup per sequence finds the chunk where
+// the running mass first exceeds u_K * S and scans it in token order for
+// the token whose cumulative mass first exceeds it.
+//
+// Kernel boundaries order the phases; no workgroup waits for another.
 
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
@@ -78,8 +78,8 @@ __global__ __launch_bounds__(kThreads) void k_rej_stats(const RejectParams p)
     const int seg = wg - row * p.segs;
     const int b = row / rows_per_seq;
     const int r = row - b * rows_per_seq;
-    unsigned len_flag = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, len_flag) : K;
+    unsigned unused = 0;
+    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, unused) : K;
     const bool is_target = r <= K;
     const int i = is_target ? r : r - (K + 1);
     const bool needed = is_target ? i <= len : i < len;
@@ -121,89 +121,30 @@ __global__ __launch_bounds__(kThreads) void k_rej_stats(const RejectParams p)
             });
     }
     const float M = block_max(m);
-    double Z = block_sum(rescale(z, m, M, p.inv_t_d));
-    float Mr = M;
+    const double Z = block_sum(rescale(z, m, M, p.inv_t_d));
+    if (threadIdx.x == 0)
+        p.partial[static_cast<int64_t>(row) * p.segs + seg] = SoftPartial{Z, M, 0};
+}
 
-    __shared__ int s_last_row, s_last_seq;
-    if (p.segs > 1) {
-        if (threadIdx.x == 0) {
-            p.partial[static_cast<int64_t>(row) * p.segs + seg] = SoftPartial{Z, M, 0};
-            s_last_row = arrive(p.row_ctr + row) == static_cast<unsigned>(p.segs - 1);
-        }
-        __syncthreads();
-        if (!s_last_row)
-            return;
-        if (threadIdx.x == 0) {
-            reset_counter(p.row_ctr + row);
-            SoftPartial *pp = p.partial + static_cast<int64_t>(row) * p.segs;
-            Mr = -__builtin_inff();
-            for (int s = 0; s < p.segs; ++s)
-                Mr = fmaxf(Mr, pp[s].m);
-            Z = 0.0;
-            for (int s = 0; s < p.segs; ++s) {
-                Z += rescale(pp[s].z, pp[s].m, Mr, p.inv_t_d);
-                pp[s] = SoftPartial{0.0, 0.0f, 0};   // the workspace is left all-zero
-            }
-        }
-    }
-    if (threadIdx.x == 0) {
-        p.rstat[row] = SoftPartial{Z, Mr, 0};
-        s_last_seq = arrive(p.seq_ctr + b) == static_cast<unsigned>(rows_per_seq - 1);
-    }
-    __syncthreads();
-    if (!s_last_seq)
-        return;
+// Row maximum and normaliser from the segment partials (same order and
+// arithmetic wherever it is called, so every caller gets identical values).
+__device__ __forceinline__ void merged_stats(const RejectParams &p, int64_t row, float &M, double &Z)
+{
+    const SoftPartial *pp = p.partial + row * p.segs;
+    M = -__builtin_inff();
+    for (int s = 0; s < p.segs; ++s)
+        M = fmaxf(M, pp[s].m);
+    Z = 0.0;
+    for (int s = 0; s < p.segs; ++s)
+        Z += rescale(pp[s].z, pp[s].m, M, p.inv_t_d);
+}
 
-    // ---- accept scan of sequence b (this workgroup finished its last row)
-    acquire_agent();
-    __shared__ int s_first_reject;
-    __shared__ unsigned s_flags;
-    if (threadIdx.x == 0) {
-        reset_counter(p.seq_ctr + b);
-        s_first_reject = len;
-        s_flags = len_flag;
-    }
-    __syncthreads();
-    const SoftPartial *rs = p.rstat + static_cast<int64_t>(b) * rows_per_seq;
-    for (int k = threadIdx.x; k < K; k += kThreads) {
-        const int x = p.draft[static_cast<int64_t>(b) * K + k];
-        const bool valid = x >= 0 && x < p.V;
-        double pk = 0.0, qk = 0.0;
-        if (k < len && valid) {
-            const E *tr = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + k) * p.row_stride;
-            const E *dr = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + k) * p.row_stride;
-            const SoftPartial st = rs[k], sd = rs[K + 1 + k];
-            pk = exp((static_cast<double>(Elem<E>::one(tr, x)) - static_cast<double>(st.m)) * p.inv_t_d) / st.z;
-            qk = exp((static_cast<double>(Elem<E>::one(dr, x)) - static_cast<double>(sd.m)) * p.inv_t_d) / sd.z;
-        }
-        if (p.p_draft)
-            p.p_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(pk);
-        if (p.q_draft)
-            p.q_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(qk);
-        if (k < len) {
-            if (!valid)
-                atomicOr(&s_flags, SV_FLAG_DRAFT_OOR);
-            const double ratio = !valid ? 0.0 : (qk > 0.0 ? pk / qk : __builtin_inf());
-            const double uk = static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]);
-            if (!(uk < ratio))
-                atomicMin(&s_first_reject, k);
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int n = s_first_reject;
-        p.accepted[b] = n;
-        p.seq_n[b] = n;
-        if (p.flags)
-            p.flags[b] = s_flags;
-        if (p.stats) {
-            stats_add(p.stats + 0, n);
-            stats_add(p.stats + 1, len);
-            stats_add(p.stats + 2, n + 1);
-            for (int k = 0; k < n; ++k)
-                stats_add(p.stats + 3 + k, 1);
-        }
-    }
+// This thread's elements [v0, v0 + cnt) of final-sample chunk cc.
+__device__ __forceinline__ void chunk_span(const RejectParams &p, int cc, int &v0, int &cnt)
+{
+    v0 = cc * kRejChunk + threadIdx.x * kChunkPerThread;
+    const int end = min(p.V, (cc + 1) * kRejChunk);
+    cnt = max(0, min(kChunkPerThread, end - v0));
 }
 
 // Per-element masses of one thread's contiguous elements [v0, v0 + cnt):
@@ -263,43 +204,108 @@ struct ChunkRows {
     }
 };
 
+// Kernel 2: one workgroup per (sequence, chunk).  Wave 0 runs the accept
+// scan of its sequence (cheap, so every chunk redoes it rather than waiting
+// for a separate launch): one lane per draft position computes p_k(x_k) and
+// q_k(x_k) in fp64 from the merged row statistics, a ballot of the
+// rejections gives the first one, n.  The workgroup then forms the final
+// sample's masses over its chunk of row pair n.  Chunk 0 also writes the
+// per-sequence outputs of the accept scan.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void k_rej_final(const RejectParams p)
+__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
 {
     const int K = p.K;
     const int rows_per_seq = 2 * K + 1;
     const int b = blockIdx.x / p.nchunks;
     const int c = blockIdx.x - b * p.nchunks;
-    unsigned unused = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, unused) : K;
-    const int n = p.seq_n[b];
-    const bool residual = n < len;
+    unsigned fl = 0;
+    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, fl) : K;
+    const int64_t row0 = static_cast<int64_t>(b) * rows_per_seq;
+    __shared__ SeqState s_seq;
 
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int n = -1;
+        bool oor = false;
+        for (int base = 0; base < K; base += 64) {
+            const int k = base + lane;
+            double pk = 0.0, qk = 0.0;
+            bool rejected = false;
+            if (k < len) {
+                const int x = p.draft[static_cast<int64_t>(b) * K + k];
+                const bool valid = x >= 0 && x < p.V;
+                oor |= !valid;
+                double ratio = 0.0;
+                if (valid) {
+                    float Mt, Md;
+                    double Zt, Zd;
+                    merged_stats(p, row0 + k, Mt, Zt);
+                    merged_stats(p, row0 + K + 1 + k, Md, Zd);
+                    const E *tr = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + k) * p.row_stride;
+                    const E *dr = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + k) * p.row_stride;
+                    pk = exp((static_cast<double>(Elem<E>::one(tr, x)) - static_cast<double>(Mt)) * p.inv_t_d) / Zt;
+                    qk = exp((static_cast<double>(Elem<E>::one(dr, x)) - static_cast<double>(Md)) * p.inv_t_d) / Zd;
+                    ratio = qk > 0.0 ? pk / qk : __builtin_inf();
+                }
+                const double uk = static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]);
+                rejected = !(uk < ratio);
+            }
+            if (c == 0 && k < K) {
+                if (p.p_draft)
+                    p.p_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(pk);
+                if (p.q_draft)
+                    p.q_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(qk);
+            }
+            const unsigned long long rej = __ballot(rejected);
+            if (n < 0 && rej)
+                n = base + __builtin_ctzll(rej);
+        }
+        if (n < 0)
+            n = len;
+        if (__ballot(oor))
+            fl |= SV_FLAG_DRAFT_OOR;
+        if (lane == 0) {
+            SeqState st{};
+            st.n = n;
+            merged_stats(p, row0 + n, st.mt, st.zt);
+            if (n < len)
+                merged_stats(p, row0 + K + 1 + n, st.md, st.zd);
+            s_seq = st;
+            if (c == 0) {
+                p.seq[b] = st;
+                p.accepted[b] = n;
+                if (p.flags)
+                    p.flags[b] = fl;
+                if (p.stats) {
+                    stats_add(p.stats + 0, n);
+                    stats_add(p.stats + 1, len);
+                    stats_add(p.stats + 2, n + 1);
+                }
+            }
+        }
+        if (c == 0 && p.stats)
+            for (int k = lane; k < n; k += 64)
+                stats_add(p.stats + 3 + k, 1);
+    }
+    __syncthreads();
+
+    const SeqState st = s_seq;
+    const int n = st.n;
     ChunkRows<E> cr;
-    const SoftPartial st = p.rstat[static_cast<int64_t>(b) * rows_per_seq + n];
     cr.pt = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + n) * p.row_stride;
-    cr.mt = st.m;
-    cr.izt = 1.0 / st.z;
+    cr.mt = st.mt;
+    cr.izt = 1.0 / st.zt;
     cr.inv_t = p.inv_t;
     cr.pd = nullptr;
     cr.md = 0.0f;
     cr.izd = 0.0;
-    if (residual) {
-        const SoftPartial sd = p.rstat[static_cast<int64_t>(b) * rows_per_seq + K + 1 + n];
+    if (n < len) {
         cr.pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
-        cr.md = sd.m;
-        cr.izd = 1.0 / sd.z;
+        cr.md = st.md;
+        cr.izd = 1.0 / st.zd;
     }
-
-    // this thread's elements of chunk cc
-    auto span = [&](int cc, int &v0, int &cnt) {
-        v0 = cc * kRejChunk + threadIdx.x * kChunkPerThread;
-        const int end = min(p.V, (cc + 1) * kRejChunk);
-        cnt = max(0, min(kChunkPerThread, end - v0));
-    };
-
     int v0, cnt;
-    span(c, v0, cnt);
+    chunk_span(p, c, v0, cnt);
     double pv[kChunkPerThread], rv[kChunkPerThread];
     cr.values(v0, cnt, pv, rv);
     double ps = 0.0, rsum = 0.0;
@@ -310,22 +316,27 @@ __global__ __launch_bounds__(kThreads) void k_rej_final(const RejectParams p)
     }
     const double Ptot = block_sum(ps);
     const double Rtot = block_sum(rsum);
-
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0)
         p.cmass[static_cast<int64_t>(b) * p.nchunks + c] = ChunkMass{Rtot, Ptot};
-        s_last = arrive(p.chunk_ctr + b) == static_cast<unsigned>(p.nchunks - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
+}
 
-    // ---- this workgroup finished the last chunk of sequence b: draw y
-    acquire_agent();
+// Kernel 3: one workgroup per sequence draws the final token y: the chunk
+// where the running mass first exceeds u_K * S, then the token inside it,
+// scanning in token order; writes the emitted tokens.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
+{
+    const int K = p.K;
+    const int b = blockIdx.x;
+    unsigned unused = 0;
+    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, unused) : K;
+    const SeqState st = p.seq[b];
+    const int n = st.n;
+    const bool residual = n < len;
+
     __shared__ int s_cs, s_use_p, s_first, s_lastpos;
     __shared__ double s_before, s_thr;
     if (threadIdx.x == 0) {
-        reset_counter(p.chunk_ctr + b);
         const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * p.nchunks;
         double SR = 0.0, SP = 0.0;
         for (int k = 0; k < p.nchunks; ++k) {
@@ -353,13 +364,6 @@ __global__ __launch_bounds__(kThreads) void k_rej_final(const RejectParams p)
             cs = lastpos;
             before = before_last;
         }
-        // every slot of this sequence has been consumed: clear it, so the
-        // workspace is all-zero when the call ends
-        for (int k = 0; k < p.nchunks; ++k)
-            p.cmass[static_cast<int64_t>(b) * p.nchunks + k] = ChunkMass{0.0, 0.0};
-        for (int k = 0; k < rows_per_seq; ++k)
-            p.rstat[static_cast<int64_t>(b) * rows_per_seq + k] = SoftPartial{0.0, 0.0f, 0};
-        p.seq_n[b] = 0;
         s_cs = cs;
         s_use_p = use_p;
         s_before = before;
@@ -368,9 +372,24 @@ __global__ __launch_bounds__(kThreads) void k_rej_final(const RejectParams p)
         s_lastpos = -1;
     }
     __syncthreads();
-    const int cs = s_cs;
+
+    ChunkRows<E> cr;
+    cr.pt = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + n) * p.row_stride;
+    cr.mt = st.mt;
+    cr.izt = 1.0 / st.zt;
+    cr.inv_t = p.inv_t;
+    cr.pd = nullptr;
+    cr.md = 0.0f;
+    cr.izd = 0.0;
+    if (residual) {
+        cr.pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
+        cr.md = st.md;
+        cr.izd = 1.0 / st.zd;
+    }
     const bool use_p = s_use_p != 0;
-    span(cs, v0, cnt);
+    int v0, cnt;
+    chunk_span(p, s_cs, v0, cnt);
+    double pv[kChunkPerThread], rv[kChunkPerThread];
     cr.values(v0, cnt, pv, rv);
     double own = 0.0;
 #pragma unroll
@@ -414,7 +433,10 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
     if (e != hipSuccess)
         return e;
     const int64_t g2 = static_cast<int64_t>(p.B) * p.nchunks;
-    hipLaunchKernelGGL(k_rej_final<E>, dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_rej_chunks<E>, dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_rej_select<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

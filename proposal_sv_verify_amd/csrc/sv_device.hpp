@@ -1,8 +1,7 @@
 // sv_device.hpp -- device helpers shared by the libspecverify kernels
 // (gfx950, wave64).  Streaming loops over logit rows with 16-byte loads,
 // (value, index) argmax combines with a total order, wave and workgroup
-// reductions, and the arrival counters of the last-arriving-workgroup
-// pattern.
+// reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -197,26 +196,10 @@ __device__ __forceinline__ double block_inclusive_scan(double x, double &total)
     return before + x;
 }
 
-// ---------------------------------------------------------------- counters
+// ---------------------------------------------------------------- misc
 
-// Arrival on a per-row or per-sequence counter.  acq_rel at agent scope:
-// the release publishes this workgroup's partial result, the acquire lets
-// the last arriver read everybody's.
-__device__ __forceinline__ unsigned arrive(unsigned *ctr)
-{
-    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void reset_counter(unsigned *ctr)
-{
-    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void acquire_agent()
-{
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
+// Accumulate into a caller's statistics counter (relaxed device-scope
+// atomic; the host reads the counters after the stream completes).
 __device__ __forceinline__ void stats_add(int64_t *p, int64_t v)
 {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -18,21 +18,30 @@ struct ArgPartial {
     int i;
 };
 
-// Per-(row, segment) softmax partial: Z relative to the segment's raw max M.
+// Per-(row, segment) softmax partial: z = sum exp((l - m) / T) over the
+// segment, m = the segment's largest raw logit.
 struct SoftPartial {
     double z;
     float m;
     int pad;
 };
 
-// Per-chunk residual masses of the final sample.
+// Per-chunk masses of the final sample.
 struct ChunkMass {
     double r;   // sum of max(0, p - q) over the chunk
     double p;   // sum of p over the chunk
 };
 
-// Greedy and tree verification: one argmax per row, then a per-sequence
-// scan by the last workgroup that finishes a row of the sequence.
+// Per-sequence state handed from the chunk kernel to the selection kernel.
+struct SeqState {
+    double zt, zd;   // normalisers of target row n and draft row n
+    float mt, md;    // raw maxima of those rows
+    int n;           // accepted drafts
+    int pad;
+};
+
+// Greedy and tree verification: a streaming argmax per (row, segment), then
+// one small per-sequence kernel.
 struct ArgVerifyParams {
     const void *logits;
     int64_t row_stride;
@@ -51,13 +60,10 @@ struct ArgVerifyParams {
     // outputs
     int32_t *accepted;
     int32_t *emitted;
-    int32_t *amax;          // [B * rows_per_seq]: argmax_out or workspace
-    int32_t amax_scratch;   // amax lives in the workspace (cleared after use)
+    int32_t *argmax_out;    // [B * rows_per_seq] or null
     uint32_t *flags;
     // workspace
-    ArgPartial *partial;    // [rows * segs] (segs > 1)
-    unsigned *row_ctr;      // [rows] (segs > 1)
-    unsigned *seq_ctr;      // [B]
+    ArgPartial *partial;    // [rows * segs]
 };
 
 hipError_t launch_greedy(const ArgVerifyParams &p, int dtype, hipStream_t s);
@@ -83,13 +89,9 @@ struct RejectParams {
     uint32_t *flags;
     int64_t *stats;
     // workspace
-    SoftPartial *partial;     // [B*(2K+1)*segs] (segs > 1)
-    SoftPartial *rstat;       // [B*(2K+1)] row max and normaliser
-    unsigned *row_ctr;        // [B*(2K+1)] (segs > 1)
-    unsigned *seq_ctr;        // [B]
-    int32_t *seq_n;           // [B] accepted count for the final-sample kernel
+    SoftPartial *partial;     // [B*(2K+1)*segs]
+    SeqState *seq;            // [B]
     ChunkMass *cmass;         // [B*nchunks]
-    unsigned *chunk_ctr;      // [B]
 };
 
 hipError_t launch_rejection(const RejectParams &p, int dtype, hipStream_t s);

@@ -28,15 +28,6 @@ def host(t):
     return t.cpu().numpy()
 
 
-def assert_workspace_zero(label=""):
-    """Every completed call leaves the (cached, shared) workspace all-zero."""
-    import proposal_sv_verify_amd as sv
-    torch.cuda.synchronize()
-    for key, buf in sv._ws_cache.items():
-        nz = int(torch.count_nonzero(buf).item())
-        assert nz == 0, "%s: workspace %s has %d non-zero bytes after the call" % (label, key, nz)
-
-
 def check_rejection(gpu, ref, label=""):
     """Decisions agree except where the oracle flags a tie; reported
     probabilities agree within 1e-5 relative.  Returns (#flagged, #mismatch)."""
