@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -63,10 +64,14 @@ int check_device()
 // ---------------------------------------------------------------- planning
 
 // Launch shape of a row-streaming kernel: every row is cut into `segs`
-// segments so that the grid holds about kTargetWorkgroups workgroups (8 per
-// CU on 256 CUs) without making segments smaller than kMinSegBytes.
+// segments.  Rows alone fill the grid once there are g_target_wgs of them
+// (8 workgroups per CU on 256 CUs); below that, the segment count is chosen
+// among those giving at least g_target_wgs workgroups (and segments of at
+// least g_min_seg_bytes) so that the workgroups fill whole rounds of the 256
+// compute units as closely as possible.
 int64_t g_target_wgs = 2048;
 int64_t g_min_seg_bytes = 32 * 1024;
+constexpr int64_t kCUs = 256;
 
 struct RowPlan {
     int segs;
@@ -75,14 +80,37 @@ struct RowPlan {
 
 RowPlan plan_rows(int64_t rows, int V, int esize)
 {
-    int64_t segs = (g_target_wgs + rows - 1) / rows;
-    const int64_t by_size = (static_cast<int64_t>(V) * esize) / g_min_seg_bytes;
-    if (segs > by_size)
-        segs = by_size;
-    if (segs < 1)
-        segs = 1;
+    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize / g_min_seg_bytes);
+    const int64_t lo = std::min(by_size, (g_target_wgs + rows - 1) / rows);
+    const int64_t hi = std::min(by_size, 2 * lo);
+    int64_t segs = lo;
+    double best = -1.0;
+    for (int64_t s = lo; s <= hi; ++s) {
+        const int64_t w = rows * s;
+        const double fill = static_cast<double>(w) / static_cast<double>((w + kCUs - 1) / kCUs * kCUs);
+        if (fill > best + 1e-9) {
+            best = fill;
+            segs = s;
+        }
+    }
     // segment length: a multiple of 64 elements so that segment starts keep
     // the 16-byte alignment of the row
+    int64_t seg_len = (V + segs - 1) / segs;
+    seg_len = (seg_len + 63) / 64 * 64;
+    segs = (V + seg_len - 1) / seg_len;
+    return RowPlan{static_cast<int>(segs), static_cast<int>(seg_len)};
+}
+
+// Launch shape of the one-wave-per-item rejection statistics kernel: each
+// row is cut into `segs` pieces so that the items about fill the wave slots
+// of the chip (4 * g_target_wgs waves: 32 per CU) in a single round, with
+// pieces of at least g_min_seg_bytes / 4 and at most kMaxSegs per row.
+RowPlan plan_items(int64_t rows, int V, int esize)
+{
+    const int64_t slots = 4 * g_target_wgs;
+    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize * 4 / g_min_seg_bytes);
+    int64_t segs = std::max<int64_t>(1, slots / rows);
+    segs = std::min<int64_t>(segs, std::min<int64_t>(by_size, sv::kMaxSegs));
     int64_t seg_len = (V + segs - 1) / segs;
     seg_len = (seg_len + 63) / 64 * 64;
     segs = (V + seg_len - 1) / seg_len;
@@ -119,7 +147,7 @@ RejLayout rej_layout(int64_t B, int64_t K, int V, const RowPlan &pl)
     L.seq = off;
     off = align_up(off + sizeof(sv::SeqState) * B);
     L.cmass = off;
-    off = align_up(off + sizeof(sv::ChunkMass) * B * nchunks);
+    off = align_up(off + sizeof(sv::ChunkMass) * B * nchunks * (sv::kRejChunk / sv::kRejSub));
     L.total = off;
     return L;
 }
@@ -351,8 +379,8 @@ size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V)
     if (B < 1 || K < 0 || V < 1)
         return 0;
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RowPlan a = plan_rows(rows, V, 2);
-    const RowPlan b = plan_rows(rows, V, 4);
+    const RowPlan a = plan_items(rows, V, 2);
+    const RowPlan b = plan_items(rows, V, 4);
     const size_t x = rej_layout(B, K, V, a).total, y = rej_layout(B, K, V, b).total;
     return x > y ? x : y;
 }
@@ -383,12 +411,12 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     if (!accepted || !emitted)
         return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_items(rows, V, esize_of(dtype));
     const RejLayout L = rej_layout(B, K, V, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
     const int nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
-    if ((st = check_grid(rows * pl.segs)) != SV_OK)
+    if ((st = check_grid((rows * pl.segs + 3) / 4)) != SV_OK)
         return st;
     if ((st = check_grid(static_cast<int64_t>(B) * nchunks)) != SV_OK)
         return st;
@@ -397,7 +425,7 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
 
     sv::RejectParams p{};
     p.target = target_logits;
-    p.draftl = draft_logits;
+    p.draftl = K > 0 ? draft_logits : target_logits;
     p.row_stride = row_stride;
     p.B = B;
     p.K = K;
@@ -405,10 +433,16 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     p.segs = pl.segs;
     p.seg_len = pl.seg_len;
     p.nchunks = nchunks;
+    {
+        const int64_t esize = esize_of(dtype);
+        p.vec_ok = !misaligned(target_logits, 16) && (K == 0 || !misaligned(draft_logits, 16)) &&
+                   (row_stride * esize) % 16 == 0 && V % (16 / esize) == 0;
+    }
     p.inv_t_d = 1.0 / static_cast<double>(temperature);
     p.inv_t = static_cast<float>(p.inv_t_d);
-    p.draft = draft;
-    p.draft_len = draft_len;
+    p.draft = K > 0 ? draft : accepted;
+    p.draft_len = draft_len ? draft_len : accepted;
+    p.has_len = draft_len != nullptr;
     p.u = uniforms;
     p.accepted = accepted;
     p.emitted = emitted;

@@ -12,9 +12,10 @@
 //          differs from the row argmax gives the first disagreement n, and
 //          the wave writes drafts 0..n-1 plus the argmax of row n;
 //  tree    ([Handbook] "Medusa"): node j is accepted when its parent is
-//          accepted and its token equals the parent row's argmax; the
-//          deepest accepted node (lowest id on ties) gives the path and the
-//          bonus token.
+//          accepted and its token equals the parent row's argmax (pointer
+//          jumping gives every node's path acceptance and depth in log N
+//          rounds); the deepest accepted node (lowest id on ties) gives the
+//          path and the bonus token.
 //
 // The kernel boundary orders the two phases: no workgroup ever waits for, or
 // fences against, another one.
@@ -44,8 +45,8 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(const ArgVerifyParams p
         const E *rp = static_cast<const E *>(p.logits) + static_cast<int64_t>(row) * p.row_stride;
         const int lo = seg * p.seg_len;
         const int hi = min(p.V, lo + p.seg_len);
-        for_each_in_segment<E, 4>(
-            rp, lo, hi,
+        stream_segment<E, 6, kThreads>(
+            rp, lo, hi, threadIdx.x,
             [&](const float(&f)[Elem<E>::kPerVec], int base) { arg_visit_vec(bv, bi, f, base); },
             [&](float x, int idx) {
                 if (x > bv) {
@@ -136,70 +137,114 @@ __global__ __launch_bounds__(kThreads) void k_greedy_scan(const ArgVerifyParams 
             stats_add(p.stats + 3 + i, 1);
 }
 
-// One workgroup per tree; thread 0 walks the nodes in id order (parents
-// precede children), the workgroup writes the outputs.
+// One workgroup per tree, all in LDS.  Acceptance and depth are prefix
+// quantities along the path to the root, computed for every node at once by
+// pointer jumping: node j starts with its parent as "up", ok(j) = its own
+// edge test, dep(j) = 1; each round folds in the values at up(j) and jumps
+// up to up(up(j)), so after ceil(log2 N) rounds ok(j) is the acceptance of
+// the whole path and dep(j) its depth.  The chosen node is the maximum of
+// (depth, -id) over accepted nodes; one thread then walks its path.
 __global__ __launch_bounds__(kThreads) void k_tree_scan(const ArgVerifyParams p)
 {
+    constexpr int kPer = (SV_MAX_TREE_NODES + kThreads - 1) / kThreads;
     __shared__ int s_t[SV_MAX_TREE_NODES];
-    __shared__ int s_depth[SV_MAX_TREE_NODES];
+    __shared__ int s_par[SV_MAX_TREE_NODES];
+    __shared__ int s_tok[SV_MAX_TREE_NODES];
+    __shared__ int s_up[SV_MAX_TREE_NODES];
+    __shared__ int s_dep[SV_MAX_TREE_NODES];
+    __shared__ unsigned char s_ok[SV_MAX_TREE_NODES];
     __shared__ int s_path[SV_MAX_TREE_NODES];
-    __shared__ unsigned char s_acc[SV_MAX_TREE_NODES];
-    __shared__ int s_best, s_bestd;
+    __shared__ unsigned s_fl;
     const int b = blockIdx.x;
     const int N = p.rows_per_seq;
-    const int *par = p.parent + static_cast<int64_t>(b) * N;
-    const int *tok = p.token + static_cast<int64_t>(b) * N;
+    if (threadIdx.x == 0)
+        s_fl = 0;
     for (int j = threadIdx.x; j < N; j += kThreads) {
-        const int t = merged_argmax(p, static_cast<int64_t>(b) * N + j);
+        const int64_t o = static_cast<int64_t>(b) * N + j;
+        const int t = merged_argmax(p, o);
         s_t[j] = t;
+        s_par[j] = p.parent[o];
+        s_tok[j] = p.token[o];
         if (p.argmax_out)
-            p.argmax_out[static_cast<int64_t>(b) * N + j] = t;
+            p.argmax_out[o] = t;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned fl = 0;
-        if (par[0] != -1)
-            fl |= SV_FLAG_BAD_PARENT;
-        s_acc[0] = 1;
-        s_depth[0] = 0;
-        int best = 0, bestd = 0;
-        for (int j = 1; j < N; ++j) {
-            const int pj = par[j];
-            const int tj = tok[j];
+    unsigned fl = 0;
+    for (int j = threadIdx.x; j < N; j += kThreads) {
+        const int pj = s_par[j];
+        int up = 0, dep = 0;
+        unsigned char ok = 1;
+        if (j == 0) {
+            if (pj != -1)
+                fl |= SV_FLAG_BAD_PARENT;
+        } else {
+            const int tj = s_tok[j];
             if (tj < 0 || tj >= p.V)
                 fl |= SV_FLAG_DRAFT_OOR;
             if (pj < 0 || pj >= j) {
                 fl |= SV_FLAG_BAD_PARENT;
-                s_acc[j] = 0;
-                s_depth[j] = 0;
-                continue;
-            }
-            const unsigned char a = s_acc[pj] && tj == s_t[pj];
-            const int dj = s_depth[pj] + 1;
-            s_acc[j] = a;
-            s_depth[j] = dj;
-            if (a && dj > bestd) {
-                bestd = dj;
-                best = j;
+                ok = 0;                       // never accepted; depth unused
+            } else {
+                up = pj;
+                dep = 1;
+                ok = tj == s_t[pj];
             }
         }
+        s_up[j] = up;
+        s_dep[j] = dep;
+        s_ok[j] = ok;
+    }
+    if (fl)
+        atomicOr(&s_fl, fl);
+    __syncthreads();
+    for (int span = 1; span < N; span <<= 1) {
+        int nup[kPer], ndep[kPer];
+        unsigned char nok[kPer];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int j = threadIdx.x + q * kThreads;
+            if (j < N) {
+                const int u = s_up[j];
+                nup[q] = s_up[u];
+                ndep[q] = s_dep[j] + s_dep[u];
+                nok[q] = s_ok[j] & s_ok[u];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int j = threadIdx.x + q * kThreads;
+            if (j < N) {
+                s_up[j] = nup[q];
+                s_dep[j] = ndep[q];
+                s_ok[j] = nok[q];
+            }
+        }
+        __syncthreads();
+    }
+    // chosen node: deepest accepted, lowest id on ties (the root always qualifies)
+    int key = 0;
+    for (int j = threadIdx.x; j < N; j += kThreads)
+        if (s_ok[j])
+            key = max(key, s_dep[j] * 2 * SV_MAX_TREE_NODES + (2 * SV_MAX_TREE_NODES - 1 - j));
+    key = block_max_int(key);
+    const int bestd = key / (2 * SV_MAX_TREE_NODES);
+    const int best = 2 * SV_MAX_TREE_NODES - 1 - (key - bestd * 2 * SV_MAX_TREE_NODES);
+    if (threadIdx.x == 0) {
         int cur = best;
         for (int dd = bestd - 1; dd >= 0; --dd) {
             s_path[dd] = cur;
-            cur = par[cur];
+            cur = s_par[cur];
         }
-        s_best = best;
-        s_bestd = bestd;
         p.accepted[b] = bestd;
         if (p.flags)
-            p.flags[b] = fl;
+            p.flags[b] = s_fl;
     }
     __syncthreads();
-    const int best = s_best, bestd = s_bestd;
     for (int j = threadIdx.x; j < N; j += kThreads) {
         const int64_t o = static_cast<int64_t>(b) * N + j;
         p.path[o] = j < bestd ? s_path[j] : -1;
-        p.emitted[o] = j < bestd ? tok[s_path[j]] : (j == bestd ? s_t[best] : -1);
+        p.emitted[o] = j < bestd ? s_tok[s_path[j]] : (j == bestd ? s_t[best] : -1);
     }
 }
 

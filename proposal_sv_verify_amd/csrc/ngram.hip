@@ -47,22 +47,6 @@ __device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int L, bool ve
     return r;
 }
 
-__device__ __forceinline__ int block_max_int(int x)
-{
-    __shared__ int s_k[kWaves];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x = max(x, __shfl_xor(x, off, 64));
-    if ((threadIdx.x & 63) == 0)
-        s_k[threadIdx.x >> 6] = x;
-    __syncthreads();
-    int m = s_k[0];
-    for (int k = 1; k < kWaves; ++k)
-        m = max(m, s_k[k]);
-    __syncthreads();
-    return m;
-}
-
 __global__ __launch_bounds__(kThreads) void k_ngram(const NgramParams p)
 {
     const int b = blockIdx.x;

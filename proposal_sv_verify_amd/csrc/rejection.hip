@@ -2,25 +2,32 @@
 // al. / Chen et al., the rule [vLLM-03] "1. principle" cites for keeping the
 // target distribution at T > 0).
 //
-// Kernel 1 (row statistics).  One workgroup per (row, segment) over the
-// K+1 target rows and K draft rows of every sequence streams the logits
-// once with 16-byte loads and keeps, per thread, an online (max, sum of exp)
-// pair: the max is taken per 8-element vector, the exp is fp32 (expf)
-// relative to the running max, sums are fp64, and a new max rescales the
-// fp64 sum with an fp64 exp.  Each segment writes (max, sum).
+// Kernel 1 (row statistics).  One wave per (row, piece) over the K+1
+// target rows and K draft rows of every sequence streams the logits once
+// with 16-byte loads (the pieces are sized so that every wave of the launch
+// is resident at once).  Each lane sums exp((l - ref) / T) against its own
+// reference, set by its first vector and moved only when a vector's terms
+// leave a wide fp32 range (the fp64 rescale almost never runs); the exp is
+// the compensated hardware exp2 (about one ulp), 8-element partial sums are
+// fp32, running sums fp64.  The wave combines its lanes onto their largest
+// reference and writes (reference, sum).
 //
-// Kernel 2 (accept scan + final-sample masses).  One workgroup per
-// (sequence, chunk).  Wave 0 merges the segment statistics of the rows it
-// needs, computes p_i(x_i) and q_i(x_i) with fp64 exp, tests u_i < p/q in
-// fp64 and finds the first rejection n.  The final token is drawn from one
-// row pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
-// zero), or p_n when every draft was accepted.  Each workgroup forms r
-// over its chunk of the row pair (fp32 exp, fp64 after) and writes the
-// chunk's masses.
+// Kernel 2 (accept scan).  One workgroup per sequence: merge the segment
+// statistics of each row in LDS, then one lane per draft position computes
+// p_k(x_k) and q_k(x_k) with fp64 exp and the test u_k < p/q in fp64; a
+// ballot of the rejections gives the first one, n.  The lane at position n
+// publishes the statistics of row pair n.
 //
-// Kernel 3 (selection).  One workgroup per sequence finds the chunk where
-// the running mass first exceeds u_K * S and scans it in token order for
-// the token whose cumulative mass first exceeds it.
+// Kernel 3 (final-sample masses).  The final token is drawn from one row
+// pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
+// zero), or p_n when every draft was accepted.  One workgroup per (sequence,
+// 4096-element chunk) forms p and r per element (fp32 exp, fp64 after);
+// each wave publishes the masses of its 1024-element sub-chunk.
+//
+// Kernel 4 (selection).  One workgroup per sequence prefix-sums the
+// sub-chunk masses to find the sub-chunk where the running mass first
+// exceeds u_K * S, then scans that sub-chunk in token order for the token
+// whose cumulative mass first exceeds it, and writes the emitted tokens.
 //
 // Kernel boundaries order the phases; no workgroup waits for another.
 
@@ -30,61 +37,81 @@
 namespace sv {
 namespace {
 
-constexpr int kChunkPerThread = kRejChunk / kThreads;   // contiguous elements per thread in kernel 2
+constexpr int kSubPerChunk = kRejChunk / kRejSub;                 // 4: one per wave
+constexpr int kChunkPerThread = kRejChunk / kThreads;             // 16 elements
+constexpr int kSubPerThread = kRejSub / kThreads;                 // 4 elements
 static_assert(kChunkPerThread * kThreads == kRejChunk, "chunk must split evenly over the threads");
+static_assert(kSubPerChunk == kWaves, "one sub-chunk per wave");
+static_assert(kSubPerThread * kThreads == kRejSub, "sub-chunk must split evenly over the threads");
 
-__device__ __forceinline__ float block_max(float x)
+// The reference of a thread's sum moves when the fp32 sum of one vector's
+// terms leaves [0, kBig] (a term above about e^44, or NaN from a -inf
+// logit): e^44 keeps every fp32 sum far from overflow.
+constexpr float kBig = 18446744073709551616.0f;   // 2^64
+
+// z * exp((m - M) / T) in fp64: moves a sum z taken against the reference m
+// onto the reference M (z == 0: nothing was summed).  Out of line: it runs
+// rarely, and inlined it would hold the fp64 exp's constants in registers
+// across the streaming loop.
+__device__ __attribute__((noinline)) double rescale_slow(double z, float m, float M, double inv_t_d)
 {
-    __shared__ float s_m[kWaves];
-    x = wave_max(x);
-    if ((threadIdx.x & 63) == 0)
-        s_m[threadIdx.x >> 6] = x;
-    __syncthreads();
-    float m = s_m[0];
-    for (int k = 1; k < kWaves; ++k)
-        m = fmaxf(m, s_m[k]);
-    __syncthreads();
-    return m;
+    return z * exp((static_cast<double>(m) - static_cast<double>(M)) * inv_t_d);
 }
 
-__device__ __forceinline__ double block_sum(double x)
+__device__ __forceinline__ double rescale(double z, float m, float M, double inv_t_d)
 {
-    __shared__ double s_s[kWaves];
-    x = wave_sum(x);
-    if ((threadIdx.x & 63) == 0)
-        s_s[threadIdx.x >> 6] = x;
-    __syncthreads();
-    double s = 0.0;
-    for (int k = 0; k < kWaves; ++k)
-        s += s_s[k];
-    __syncthreads();
+    return z != 0.0 ? rescale_slow(z, m, M, inv_t_d) : 0.0;
+}
+
+// Sum of e^((l - ref) / T) over n values, moving (ref, z) first when a value
+// exceeds ref; -inf values add 0.  The careful path of the statistics loop.
+template <bool kUnitT, int n>
+__device__ __forceinline__ float careful_sum(const float (&f)[n], float &ref, double &z, float inv_t, double inv_t_d)
+{
+    float vm = f[0];
+#pragma unroll
+    for (int j = 1; j < n; ++j)
+        vm = fmaxf(vm, f[j]);
+    if (vm > ref) {
+        z = rescale(z, ref, vm, inv_t_d);
+        ref = vm;
+    }
+    float s = 0.0f;
+    if (ref != -__builtin_inff()) {
+#pragma unroll
+        for (int j = 0; j < n; ++j)
+            s += exp_cz(kUnitT ? f[j] - ref : (f[j] - ref) * inv_t);
+    }
     return s;
 }
 
-// sum_k z_k * exp((m_k - M) / T) over partials (m_k, z_k) with M = max m_k;
-// partials with z_k == 0 saw no element.
-__device__ __forceinline__ double rescale(double z, float m, float M, double inv_t_d)
+// One wave per work item (row, piece); a workgroup carries four items.
+// Each lane sums e^((l - ref) / T) against its own reference, which starts
+// at -inf (so its first vector takes the careful path and sets it) and
+// moves only through the careful path; the fast path is the compensated
+// exp and an fp32 sum per vector, accumulated in fp64.  The reference need
+// not be the true maximum: any value within e^44 of it keeps the sums exact
+// to fp32 rounding, and the row merge accepts any reference.
+template <typename E, bool kUnitT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_stats(const RejectParams p)
 {
-    return z != 0.0 ? z * exp((static_cast<double>(m) - static_cast<double>(M)) * inv_t_d) : 0.0;
-}
-
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_rej_stats(const RejectParams p)
-{
+    const int lane = threadIdx.x & 63;
     const int K = p.K;
     const int rows_per_seq = 2 * K + 1;
-    const int wg = blockIdx.x;
-    const int row = wg / p.segs;
-    const int seg = wg - row * p.segs;
-    const int b = row / rows_per_seq;
-    const int r = row - b * rows_per_seq;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (item >= static_cast<int64_t>(p.B) * rows_per_seq * p.segs)
+        return;
+    const int64_t row = item / p.segs;
+    const int seg = static_cast<int>(item - row * p.segs);
+    const int b = static_cast<int>(row / rows_per_seq);
+    const int r = static_cast<int>(row - static_cast<int64_t>(b) * rows_per_seq);
     unsigned unused = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, unused) : K;
+    const int len = p.has_len ? clamp_len(p.draft_len[b], K, unused) : K;
     const bool is_target = r <= K;
     const int i = is_target ? r : r - (K + 1);
     const bool needed = is_target ? i <= len : i < len;
 
-    float m = -__builtin_inff();
+    float ref = -__builtin_inff();
     double z = 0.0;
     if (needed) {
         const E *rp = is_target
@@ -94,346 +121,465 @@ __global__ __launch_bounds__(kThreads) void k_rej_stats(const RejectParams p)
         const int hi = min(p.V, lo + p.seg_len);
         const float inv_t = p.inv_t;
         const double inv_t_d = p.inv_t_d;
-        for_each_in_segment<E, 4>(
-            rp, lo, hi,
+        auto arg = [&](float x) { return kUnitT ? x - ref : (x - ref) * inv_t; };
+        stream_segment<E, 4, 64>(
+            rp, lo, hi, lane,
             [&](const float(&f)[Elem<E>::kPerVec], int) {
                 constexpr int PV = Elem<E>::kPerVec;
-                float vm = f[0];
+                float s = exp_c(arg(f[0]));
 #pragma unroll
                 for (int j = 1; j < PV; ++j)
-                    vm = fmaxf(vm, f[j]);
-                if (vm > m) {
-                    z = rescale(z, m, vm, inv_t_d);
-                    m = vm;
-                }
-                float s = 0.0f;
-#pragma unroll
-                for (int j = 0; j < PV; ++j)
-                    s += expf((f[j] - m) * inv_t);
+                    s += exp_c(arg(f[j]));
+                if (!(s <= kBig))
+                    s = careful_sum<kUnitT>(f, ref, z, inv_t, inv_t_d);
                 z += static_cast<double>(s);
             },
             [&](float x, int) {
-                if (x > m) {
-                    z = rescale(z, m, x, inv_t_d);
-                    m = x;
+                float s = exp_c(arg(x));
+                if (!(s <= kBig)) {
+                    const float f[1] = {x};
+                    s = careful_sum<kUnitT>(f, ref, z, inv_t, inv_t_d);
                 }
-                z += static_cast<double>(expf((x - m) * inv_t));
+                z += static_cast<double>(s);
             });
     }
-    const float M = block_max(m);
-    const double Z = block_sum(rescale(z, m, M, p.inv_t_d));
-    if (threadIdx.x == 0)
-        p.partial[static_cast<int64_t>(row) * p.segs + seg] = SoftPartial{Z, M, 0};
+    // onto the item's largest reference: one fp64 rescale per lane (none for
+    // the lane holding it), then a wave sum
+    const float M = wave_max(ref);
+    const double zz = wave_sum(ref == M ? z : rescale(z, ref, M, p.inv_t_d));
+    if (lane == 0)
+        p.partial[item] = SoftPartial{zz, M, 0};
 }
 
-// Row maximum and normaliser from the segment partials (same order and
-// arithmetic wherever it is called, so every caller gets identical values).
-__device__ __forceinline__ void merged_stats(const RejectParams &p, int64_t row, float &M, double &Z)
-{
-    const SoftPartial *pp = p.partial + row * p.segs;
-    M = -__builtin_inff();
-    for (int s = 0; s < p.segs; ++s)
-        M = fmaxf(M, pp[s].m);
-    Z = 0.0;
-    for (int s = 0; s < p.segs; ++s)
-        Z += rescale(pp[s].z, pp[s].m, M, p.inv_t_d);
-}
+// The small kernels below issue every load of a phase before using any of
+// them (addresses are clamped in bounds instead of guarded by branches, the
+// values outside the wanted range are dropped after loading): a load consumed
+// inside a branch or loop is waited for on the spot, and each such wait costs
+// a full memory round trip.
 
-// This thread's elements [v0, v0 + cnt) of final-sample chunk cc.
-__device__ __forceinline__ void chunk_span(const RejectParams &p, int cc, int &v0, int &cnt)
-{
-    v0 = cc * kRejChunk + threadIdx.x * kChunkPerThread;
-    const int end = min(p.V, (cc + 1) * kRejChunk);
-    cnt = max(0, min(kChunkPerThread, end - v0));
-}
+// Kernel 2: one workgroup per sequence, draft positions in blocks of 64.
+// A block needs the statistics of 64 target rows and 64 draft rows: their
+// segment partials are staged in LDS, each row's maximum is found, every
+// partial is moved onto it (the fp64 rescales run in parallel, one thread per
+// partial) and the row sums are formed; then wave 0 runs the accept test with
+// one lane per position.
+constexpr int kScanRows = 128;
+constexpr int kScanPer = kScanRows * kMaxSegs / kThreads;      // partials per thread, at most
 
-// Per-element masses of one thread's contiguous elements [v0, v0 + cnt):
-// p_v = exp((l_v - M) / T) / Z (fp32 exp, fp64 after) and, after a
-// rejection, r_v = max(0, p_v - q_v).
 template <typename E>
-struct ChunkRows {
-    const E *pt;
-    const E *pd;        // null when sampling the bonus
-    float mt, md;
-    double izt, izd;
-    float inv_t;
-
-    __device__ __forceinline__ void load(const E *row, int v0, int cnt, float (&f)[kChunkPerThread]) const
-    {
-        constexpr int PV = Elem<E>::kPerVec;
-        const E *src = row + v0;
-        if (cnt == kChunkPerThread && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-            const u32x4 *vp = reinterpret_cast<const u32x4 *>(src);
-#pragma unroll
-            for (int q = 0; q < kChunkPerThread / PV; ++q) {
-                float g[PV];
-                Elem<E>::unpack(vp[q], g);
-#pragma unroll
-                for (int j = 0; j < PV; ++j)
-                    f[q * PV + j] = g[j];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kChunkPerThread; ++j)
-                f[j] = j < cnt ? Elem<E>::one(src, j) : 0.0f;
-        }
-    }
-
-    // p and r for every element; entries j >= cnt are zero
-    __device__ __forceinline__ void values(int v0, int cnt, double (&pv)[kChunkPerThread],
-                                           double (&rv)[kChunkPerThread]) const
-    {
-        float ft[kChunkPerThread];
-        load(pt, v0, cnt, ft);
-        float fd[kChunkPerThread];
-        if (pd)
-            load(pd, v0, cnt, fd);
-#pragma unroll
-        for (int j = 0; j < kChunkPerThread; ++j) {
-            pv[j] = 0.0;
-            rv[j] = 0.0;
-            if (j < cnt) {
-                const double a = static_cast<double>(expf((ft[j] - mt) * inv_t)) * izt;
-                pv[j] = a;
-                if (pd) {
-                    const double d = a - static_cast<double>(expf((fd[j] - md) * inv_t)) * izd;
-                    rv[j] = d > 0.0 ? d : 0.0;
-                }
-            }
-        }
-    }
-};
-
-// Kernel 2: one workgroup per (sequence, chunk).  Wave 0 runs the accept
-// scan of its sequence (cheap, so every chunk redoes it rather than waiting
-// for a separate launch): one lane per draft position computes p_k(x_k) and
-// q_k(x_k) in fp64 from the merged row statistics, a ballot of the
-// rejections gives the first one, n.  The workgroup then forms the final
-// sample's masses over its chunk of row pair n.  Chunk 0 also writes the
-// per-sequence outputs of the accept scan.
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
+__global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
 {
+    __shared__ float s_m[kScanRows * kMaxSegs];
+    __shared__ double s_z[kScanRows * kMaxSegs];
+    __shared__ float s_M[kScanRows];
+    __shared__ double s_Z[kScanRows];
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const bool lead = t < 64;                 // wave 0 runs the per-position test
     const int K = p.K;
-    const int rows_per_seq = 2 * K + 1;
-    const int b = blockIdx.x / p.nchunks;
-    const int c = blockIdx.x - b * p.nchunks;
+    const int segs = p.segs;
+    const int64_t row0 = static_cast<int64_t>(b) * (2 * K + 1);
+    const int nparts = kScanRows * segs;
+    int n = -1;                               // known to wave 0
+    bool oor = false;
     unsigned fl = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, fl) : K;
-    const int64_t row0 = static_cast<int64_t>(b) * rows_per_seq;
-    __shared__ SeqState s_seq;
-
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int n = -1;
-        bool oor = false;
-        for (int base = 0; base < K; base += 64) {
-            const int k = base + lane;
+    int len = K;
+    for (int base = 0; base <= K; base += 64) {
+        const int k = base + lane;
+        const int kc = max(0, min(k, K - 1));
+        // the draft token first, so its logits can follow it (every wave
+        // loads them; wave 0 uses them)
+        const int x = p.draft[static_cast<int64_t>(b) * K + kc];
+        // every thread: its partials of target rows base.. and draft rows base..
+        SoftPartial q[kScanPer];
+#pragma unroll
+        for (int j = 0; j < kScanPer; ++j) {
+            const int idx = min(t + j * kThreads, nparts - 1);
+            const int rr = idx / segs;
+            const int s = idx - rr * segs;
+            const int kk = base + (rr & 63);
+            const int ri = rr < 64 ? min(kk, K) : K + 1 + min(kk, K - 1);   // a row of this sequence
+            q[j] = p.partial[(row0 + ri) * segs + s];
+        }
+        const bool valid = K > 0 && x >= 0 && x < p.V;
+        const int xc = valid ? x : 0;
+        const float lt = Elem<E>::one(static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + kc) * p.row_stride, xc);
+        const float ld = Elem<E>::one(static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + kc) * p.row_stride, xc);
+        const int len_raw = p.draft_len[b];
+        len = p.has_len ? clamp_len(len_raw, K, fl) : K;
+#pragma unroll
+        for (int j = 0; j < kScanPer; ++j) {
+            const int idx = t + j * kThreads;
+            if (idx < nparts) {
+                const int rr = idx / segs;
+                const int kk = base + (rr & 63);
+                const bool use = rr < 64 ? kk <= len : kk < len;
+                s_m[idx] = use ? q[j].m : -__builtin_inff();
+                s_z[idx] = use ? q[j].z : 0.0;
+            }
+        }
+        __syncthreads();
+        if (t < kScanRows) {
+            float M = -__builtin_inff();
+            for (int s = 0; s < segs; ++s)
+                M = fmaxf(M, s_m[t * segs + s]);
+            s_M[t] = M;
+        }
+        __syncthreads();
+        for (int idx = t; idx < nparts; idx += kThreads) {
+            const float m = s_m[idx];
+            const float M = s_M[idx / segs];
+            if (m != M)
+                s_z[idx] = rescale(s_z[idx], m, M, p.inv_t_d);
+        }
+        __syncthreads();
+        if (t < kScanRows) {
+            double Z = 0.0;
+            for (int s = 0; s < segs; ++s)
+                Z += s_z[t * segs + s];
+            s_Z[t] = Z;
+        }
+        __syncthreads();
+        if (lead) {
+            oor |= k < len && !valid;
+            const double zt = s_Z[lane], zd = s_Z[64 + lane];
+            const float mt = s_M[lane], md = s_M[64 + lane];
             double pk = 0.0, qk = 0.0;
             bool rejected = false;
             if (k < len) {
-                const int x = p.draft[static_cast<int64_t>(b) * K + k];
-                const bool valid = x >= 0 && x < p.V;
-                oor |= !valid;
                 double ratio = 0.0;
                 if (valid) {
-                    float Mt, Md;
-                    double Zt, Zd;
-                    merged_stats(p, row0 + k, Mt, Zt);
-                    merged_stats(p, row0 + K + 1 + k, Md, Zd);
-                    const E *tr = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + k) * p.row_stride;
-                    const E *dr = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + k) * p.row_stride;
-                    pk = exp((static_cast<double>(Elem<E>::one(tr, x)) - static_cast<double>(Mt)) * p.inv_t_d) / Zt;
-                    qk = exp((static_cast<double>(Elem<E>::one(dr, x)) - static_cast<double>(Md)) * p.inv_t_d) / Zd;
+                    pk = exp((static_cast<double>(lt) - static_cast<double>(mt)) * p.inv_t_d) / zt;
+                    qk = exp((static_cast<double>(ld) - static_cast<double>(md)) * p.inv_t_d) / zd;
                     ratio = qk > 0.0 ? pk / qk : __builtin_inf();
                 }
-                const double uk = static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]);
-                rejected = !(uk < ratio);
+                rejected = !(static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]) < ratio);
             }
-            if (c == 0 && k < K) {
+            if (k < K) {
                 if (p.p_draft)
                     p.p_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(pk);
                 if (p.q_draft)
                     p.q_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(qk);
             }
             const unsigned long long rej = __ballot(rejected);
-            if (n < 0 && rej)
-                n = base + __builtin_ctzll(rej);
-        }
-        if (n < 0)
-            n = len;
-        if (__ballot(oor))
-            fl |= SV_FLAG_DRAFT_OOR;
-        if (lane == 0) {
-            SeqState st{};
-            st.n = n;
-            merged_stats(p, row0 + n, st.mt, st.zt);
-            if (n < len)
-                merged_stats(p, row0 + K + 1 + n, st.md, st.zd);
-            s_seq = st;
-            if (c == 0) {
-                p.seq[b] = st;
-                p.accepted[b] = n;
-                if (p.flags)
-                    p.flags[b] = fl;
-                if (p.stats) {
-                    stats_add(p.stats + 0, n);
-                    stats_add(p.stats + 1, len);
-                    stats_add(p.stats + 2, n + 1);
-                }
+            int here = -1;
+            if (n < 0) {
+                if (rej)
+                    here = base + __builtin_ctzll(rej);
+                else if (len < base + 64)
+                    here = len;               // every draft accepted: the bonus row
             }
+            if (here >= 0 && k == here) {
+                SeqState sq{};
+                sq.n = here;
+                sq.zt = zt;
+                sq.mt = mt;
+                if (here < len) {
+                    sq.zd = zd;
+                    sq.md = md;
+                }
+                p.seq[b] = sq;
+            }
+            if (n < 0)
+                n = here;
         }
-        if (c == 0 && p.stats)
-            for (int k = lane; k < n; k += 64)
-                stats_add(p.stats + 3 + k, 1);
+        __syncthreads();                      // LDS is restaged by the next block
     }
-    __syncthreads();
-
-    const SeqState st = s_seq;
-    const int n = st.n;
-    ChunkRows<E> cr;
-    cr.pt = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + n) * p.row_stride;
-    cr.mt = st.mt;
-    cr.izt = 1.0 / st.zt;
-    cr.inv_t = p.inv_t;
-    cr.pd = nullptr;
-    cr.md = 0.0f;
-    cr.izd = 0.0;
-    if (n < len) {
-        cr.pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
-        cr.md = st.md;
-        cr.izd = 1.0 / st.zd;
+    if (!lead)
+        return;
+    if (__ballot(oor))
+        fl |= SV_FLAG_DRAFT_OOR;
+    if (lane == 0) {
+        p.accepted[b] = n;
+        if (p.flags)
+            p.flags[b] = fl;
+        if (p.stats) {
+            stats_add(p.stats + 0, n);
+            stats_add(p.stats + 1, len);
+            stats_add(p.stats + 2, n + 1);
+        }
     }
-    int v0, cnt;
-    chunk_span(p, c, v0, cnt);
-    double pv[kChunkPerThread], rv[kChunkPerThread];
-    cr.values(v0, cnt, pv, rv);
-    double ps = 0.0, rsum = 0.0;
-#pragma unroll
-    for (int j = 0; j < kChunkPerThread; ++j) {
-        ps += pv[j];
-        rsum += rv[j];
-    }
-    const double Ptot = block_sum(ps);
-    const double Rtot = block_sum(rsum);
-    if (threadIdx.x == 0)
-        p.cmass[static_cast<int64_t>(b) * p.nchunks + c] = ChunkMass{Rtot, Ptot};
+    if (p.stats)
+        for (int k = lane; k < n; k += 64)
+            stats_add(p.stats + 3 + k, 1);
 }
 
-// Kernel 3: one workgroup per sequence draws the final token y: the chunk
-// where the running mass first exceeds u_K * S, then the token inside it,
-// scanning in token order; writes the emitted tokens.
+// kN consecutive elements [v0, v0 + kN) of a row, loaded before use.  kVec:
+// the row is a whole number of aligned 16-byte vectors, so each vector of
+// the slice lies wholly inside the row or wholly past it, and one past it
+// loads the row's last vector instead.  Otherwise elements are loaded one by
+// one with the index clamped to V - 1.  Values past the row are garbage for
+// the caller to drop.
+template <typename E, int kN, bool kVec>
+struct Slice {
+    static constexpr int PV = Elem<E>::kPerVec;
+    static constexpr int NV = kVec ? kN / PV : 1;
+    static constexpr int NE = kVec ? 1 : kN;
+    static_assert(!kVec || kN % PV == 0, "vector slices hold whole vectors");
+    u32x4 v[NV];
+    E e[NE];
+
+    __device__ __forceinline__ void fetch(const E *row, int v0, int V)
+    {
+        if constexpr (kVec) {
+            const u32x4 *vp = reinterpret_cast<const u32x4 *>(row);
+            const int last = V / PV - 1;
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+                v[q] = vp[min(v0 / PV + q, last)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE; ++j)
+                e[j] = row[min(v0 + j, V - 1)];
+        }
+    }
+
+    __device__ __forceinline__ void widen(float (&f)[kN]) const
+    {
+        if constexpr (kVec) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                float g[PV];
+                Elem<E>::unpack(v[q], g);
+#pragma unroll
+                for (int j = 0; j < PV; ++j)
+                    f[q * PV + j] = g[j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE; ++j)
+                f[j] = Elem<E>::widen(e[j]);
+        }
+    }
+};
+
+// The rows of the final sample and the per-element masses over a thread's
+// kN contiguous elements [v0, v0 + cnt).
+template <typename E>
+struct SampleRows {
+    const E *pt;
+    const E *pd;        // the target row again when sampling the bonus
+    bool residual;      // a draft row is present: r is formed
+    float mt, md;
+    double izt, izd;
+    float inv_t;
+    int V;
+
+    __device__ __forceinline__ SampleRows(const RejectParams &p, int b, int len, const SeqState &st)
+    {
+        const int K = p.K, n = st.n;
+        pt = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + n) * p.row_stride;
+        mt = st.mt;
+        izt = 1.0 / st.zt;
+        inv_t = p.inv_t;
+        V = p.V;
+        residual = n < len;
+        pd = pt;
+        md = 0.0f;
+        izd = 0.0;
+        if (residual) {
+            pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
+            md = st.md;
+            izd = 1.0 / st.zd;
+        }
+    }
+
+    // visit(j, p_j, r_j) for j < cnt in order: p_j = exp((l - M) / T) / Z
+    // (fp32 exp, fp64 after); after a rejection r_j = max(0, p_j - q_j),
+    // with no draft row r_j = 0.  Both rows are loaded before either is used.
+    template <int kN, bool kVec, typename F>
+    __device__ __forceinline__ void visit(int v0, int cnt, F &&f) const
+    {
+        Slice<E, kN, kVec> st, sd;
+        st.fetch(pt, v0, V);
+        sd.fetch(pd, v0, V);
+        float ft[kN], fd[kN];
+        st.widen(ft);
+        sd.widen(fd);
+#pragma unroll
+        for (int j = 0; j < kN; ++j) {
+            if (j < cnt) {
+                const double a = static_cast<double>(exp_cz((ft[j] - mt) * inv_t)) * izt;
+                double r = 0.0;
+                if (residual) {
+                    const double d = a - static_cast<double>(exp_cz((fd[j] - md) * inv_t)) * izd;
+                    r = d > 0.0 ? d : 0.0;
+                }
+                f(j, a, r);
+            }
+        }
+    }
+};
+
+// Kernel 3: one workgroup per (sequence, chunk); two memory rounds (the
+// sequence state, then both rows' slices).
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
+{
+    const int b = blockIdx.x / p.nchunks;
+    const int c = blockIdx.x - b * p.nchunks;
+    const int len_raw = p.draft_len[b];
+    const SeqState st = p.seq[b];
+    unsigned unused = 0;
+    const int len = p.has_len ? clamp_len(len_raw, p.K, unused) : p.K;
+    const SampleRows<E> sr(p, b, len, st);
+    const int v0 = c * kRejChunk + threadIdx.x * kChunkPerThread;
+    const int cnt = max(0, min(kChunkPerThread, p.V - v0));
+    double ps = 0.0, rs = 0.0;
+    sr.template visit<kChunkPerThread, kVec>(v0, cnt, [&](int, double a, double r) {
+        ps += a;
+        rs += r;
+    });
+    ps = wave_sum(ps);
+    rs = wave_sum(rs);
+    if ((threadIdx.x & 63) == 0)
+        p.cmass[(static_cast<int64_t>(b) * p.nchunks + c) * kSubPerChunk + (threadIdx.x >> 6)] =
+            ChunkMass{rs, ps};
+}
+
+// Kernel 4: one workgroup per sequence, two memory rounds.  Round 1 loads
+// everything that does not depend on the chosen sub-chunk: the sequence
+// state, u_K, the sequence's sub-chunk masses (kept in registers, and staged
+// in LDS when they fit) and the drafts it re-emits.  Round 2 loads the one
+// sub-chunk where the running mass crosses u_K * S.
+constexpr int kSelStage = 2048;                   // sub-chunk masses staged in LDS (V up to 2M)
+constexpr int kSelPer = kSelStage / kThreads;     // masses per thread held in registers
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
 {
+    __shared__ ChunkMass s_cm[kSelStage];
+    __shared__ double s_before;
     const int K = p.K;
     const int b = blockIdx.x;
-    unsigned unused = 0;
-    const int len = p.draft_len ? clamp_len(p.draft_len[b], K, unused) : K;
+    const int t = threadIdx.x;
+    const int len_raw = p.draft_len[b];
     const SeqState st = p.seq[b];
+    const float ufin = p.u[static_cast<int64_t>(b) * (K + 1) + K];
+    const int nsub = p.nchunks * kSubPerChunk;
+    const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * nsub;
+    const bool staged = nsub <= kSelStage;
+    const int per = (nsub + kThreads - 1) / kThreads;      // sub-chunks per thread
+    const int k0 = min(nsub, t * per);
+    const int k1 = min(nsub, k0 + per);
+    ChunkMass mine[kSelPer];
+    if (staged) {
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j)
+            mine[j] = cm[min(k0 + j, nsub - 1)];
+    }
+    const int *d = p.draft + static_cast<int64_t>(b) * K;
+    const int d_own = d[max(0, min(t, K - 1))];
+    double myr = 0.0, myp = 0.0;
+    if (staged) {
+#pragma unroll
+        for (int j = 0; j < kSelPer; ++j) {
+            if (k0 + j < k1) {
+                s_cm[k0 + j] = mine[j];
+                myr += mine[j].r;
+                myp += mine[j].p;
+            }
+        }
+    } else {
+        for (int k = k0; k < k1; ++k) {
+            const ChunkMass q = cm[k];
+            myr += q.r;
+            myp += q.p;
+        }
+    }
+    unsigned unused = 0;
+    const int len = p.has_len ? clamp_len(len_raw, K, unused) : K;
     const int n = st.n;
     const bool residual = n < len;
-
-    __shared__ int s_cs, s_use_p, s_first, s_lastpos;
-    __shared__ double s_before, s_thr;
-    if (threadIdx.x == 0) {
-        const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * p.nchunks;
-        double SR = 0.0, SP = 0.0;
-        for (int k = 0; k < p.nchunks; ++k) {
-            SR += cm[k].r;
-            SP += cm[k].p;
-        }
-        const int use_p = !residual || SR == 0.0;
-        const double S = use_p ? SP : SR;
-        const double thr = static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + K]) * S;
-        int cs = -1, lastpos = 0;
-        double before = 0.0, run = 0.0, before_last = 0.0;
-        for (int k = 0; k < p.nchunks; ++k) {
-            const double X = use_p ? cm[k].p : cm[k].r;
-            if (X > 0.0) {
-                lastpos = k;
-                before_last = run;
-            }
-            if (cs < 0 && run + X > thr) {
+    // (the barriers inside the scans also publish s_cm)
+    double SR, SP;
+    const double inclr = block_inclusive_scan(myr, SR);
+    const double inclp = block_inclusive_scan(myp, SP);
+    const bool use_p = !residual || SR == 0.0;
+    const double S = use_p ? SP : SR;
+    const double thr = static_cast<double>(ufin) * S;
+    int first_cs, last_c;
+    auto mass = [&](int k) {
+        const ChunkMass q = staged ? s_cm[k] : cm[k];
+        return use_p ? q.p : q.r;
+    };
+    {
+        double run = use_p ? inclp - myp : inclr - myr;
+        int cs = kIdxNone, lastc = -1;
+        for (int k = k0; k < k1; ++k) {
+            const double X = mass(k);
+            if (X > 0.0)
+                lastc = k;
+            if (cs == kIdxNone && run + X > thr)
                 cs = k;
-                before = run;
-            }
             run += X;
         }
-        if (cs < 0) {           // rounding left u*S at or past the total
-            cs = lastpos;
-            before = before_last;
-        }
-        s_cs = cs;
-        s_use_p = use_p;
-        s_before = before;
-        s_thr = thr;
-        s_first = kIdxNone;
-        s_lastpos = -1;
+        block_first_last(cs != kIdxNone, cs, lastc >= 0, lastc, first_cs, last_c);
+    }
+    // rounding can leave u*S at or past the total: take the last sub-chunk with mass
+    const int cs = first_cs != kIdxNone ? first_cs : max(last_c, 0);
+    if (cs >= k0 && cs < k1) {                    // the owner knows the mass before cs
+        double run = use_p ? inclp - myp : inclr - myr;
+        for (int k = k0; k < cs; ++k)             // only when a thread owns several
+            run += mass(k);
+        s_before = run;
     }
     __syncthreads();
 
-    ChunkRows<E> cr;
-    cr.pt = static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + n) * p.row_stride;
-    cr.mt = st.mt;
-    cr.izt = 1.0 / st.zt;
-    cr.inv_t = p.inv_t;
-    cr.pd = nullptr;
-    cr.md = 0.0f;
-    cr.izd = 0.0;
-    if (residual) {
-        cr.pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
-        cr.md = st.md;
-        cr.izd = 1.0 / st.zd;
-    }
-    const bool use_p = s_use_p != 0;
-    int v0, cnt;
-    chunk_span(p, s_cs, v0, cnt);
-    double pv[kChunkPerThread], rv[kChunkPerThread];
-    cr.values(v0, cnt, pv, rv);
+    const SampleRows<E> sr(p, b, len, st);
+    const int v0 = cs * kRejSub + t * kSubPerThread;
+    const int cnt = max(0, min(kSubPerThread, p.V - v0));
+    double xs[kSubPerThread];
     double own = 0.0;
-#pragma unroll
-    for (int j = 0; j < kChunkPerThread; ++j)
-        own += use_p ? pv[j] : rv[j];
+    sr.template visit<kSubPerThread, false>(v0, cnt, [&](int j, double a, double r) {
+        xs[j] = use_p ? a : r;
+        own += xs[j];
+    });
     double tot;
     const double incl = block_inclusive_scan(own, tot);
     double cum = s_before + (incl - own);
-    const double thr = s_thr;
     int first = kIdxNone, lastpos = -1;
 #pragma unroll
-    for (int j = 0; j < kChunkPerThread; ++j) {
-        const double x = use_p ? pv[j] : rv[j];
-        cum += x;
-        if (j < cnt && x > 0.0) {
-            lastpos = v0 + j;
-            if (first == kIdxNone && cum > thr)
-                first = v0 + j;
+    for (int j = 0; j < kSubPerThread; ++j) {
+        if (j < cnt) {
+            const double x = xs[j];
+            cum += x;
+            if (x > 0.0) {
+                lastpos = v0 + j;
+                if (first == kIdxNone && cum > thr)
+                    first = v0 + j;
+            }
         }
     }
-    if (first != kIdxNone)
-        atomicMin(&s_first, first);
-    if (lastpos >= 0)
-        atomicMax(&s_lastpos, lastpos);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int y = s_first != kIdxNone ? s_first : s_lastpos;
-        int *e = p.emitted + static_cast<int64_t>(b) * (K + 1);
-        const int *d = p.draft + static_cast<int64_t>(b) * K;
-        for (int k = 0; k <= K; ++k)
-            e[k] = k < n ? d[k] : (k == n ? y : -1);
-    }
+    int yf, yl;
+    block_first_last(first != kIdxNone, first, lastpos >= 0, lastpos, yf, yl);
+    const int y = yf != kIdxNone ? yf : yl;
+    int *e = p.emitted + static_cast<int64_t>(b) * (K + 1);
+    for (int k = t; k <= K; k += kThreads)
+        e[k] = k < n ? (k == t ? d_own : d[k]) : (k == n ? y : -1);
 }
 
 template <typename E>
 hipError_t launch_typed(const RejectParams &p, hipStream_t s)
 {
-    const int64_t g1 = static_cast<int64_t>(p.B) * (2 * p.K + 1) * p.segs;
-    hipLaunchKernelGGL(k_rej_stats<E>, dim3(static_cast<unsigned>(g1)), dim3(kThreads), 0, s, p);
+    const int64_t items = static_cast<int64_t>(p.B) * (2 * p.K + 1) * p.segs;
+    const dim3 g1(static_cast<unsigned>((items + kWaves - 1) / kWaves));
+    if (p.inv_t == 1.0f)
+        hipLaunchKernelGGL((k_rej_stats<E, true>), g1, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_rej_stats<E, false>), g1, dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int64_t g2 = static_cast<int64_t>(p.B) * p.nchunks;
-    hipLaunchKernelGGL(k_rej_chunks<E>, dim3(static_cast<unsigned>(g2)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_rej_scan<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
+    if (p.vec_ok)
+        hipLaunchKernelGGL((k_rej_chunks<E, true>), g3, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_rej_chunks<E, false>), g3, dim3(kThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     hipLaunchKernelGGL(k_rej_select<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);

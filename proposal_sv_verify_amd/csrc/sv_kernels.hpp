@@ -9,8 +9,14 @@
 namespace sv {
 
 // Elements of one final-sample chunk in rejection sampling (16 per thread of
-// a 256-thread workgroup).
+// a 256-thread workgroup); each wave's quarter of a chunk (a sub-chunk of
+// 1024 elements) publishes its own masses.
 constexpr int kRejChunk = 4096;
+constexpr int kRejSub = 1024;
+
+// Most segments a rejection-sampling row is cut into (the merge of a row's
+// segment partials loads them all at once).
+constexpr int kMaxSegs = 16;
 
 // Per-(row, segment) argmax partial.
 struct ArgPartial {
@@ -77,10 +83,18 @@ struct RejectParams {
     int32_t B, K, V;
     int32_t segs, seg_len;
     int32_t nchunks;          // ceil(V / kRejChunk)
+    int32_t vec_ok;           // both logit tensors 16-byte aligned, rows a whole
+                              // number of 16-byte vectors and V a multiple of
+                              // the elements per vector
     float inv_t;
     double inv_t_d;
+    // draft, draftl and draft_len always point at valid memory, so kernels can
+    // load from them unconditionally: with K == 0 draft and draftl stand in
+    // for nothing (any int array, the target logits), and without lengths
+    // (has_len == 0) draft_len is any int array of B entries, ignored.
     const int32_t *draft;
     const int32_t *draft_len;
+    int32_t has_len;
     const float *u;
     int32_t *accepted;
     int32_t *emitted;
@@ -91,7 +105,7 @@ struct RejectParams {
     // workspace
     SoftPartial *partial;     // [B*(2K+1)*segs]
     SeqState *seq;            // [B]
-    ChunkMass *cmass;         // [B*nchunks]
+    ChunkMass *cmass;         // [B*nchunks*4] masses per sub-chunk
 };
 
 hipError_t launch_rejection(const RejectParams &p, int dtype, hipStream_t s);

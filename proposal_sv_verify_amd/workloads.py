@@ -47,7 +47,7 @@ def seed_for(config_number: int, salt: int = 0) -> int:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bf16, nearest-even, returning uint16 bit patterns.
-    Inputs here are finite; NaN handling is not needed."""
+    Finite values and +-inf map correctly; NaN handling is not needed."""
     bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
     return ((bits + bias) >> np.uint32(16)).astype(np.uint16)
@@ -136,11 +136,25 @@ def gumbel_max_sample(logits_f32: np.ndarray, temperature: float, rng) -> np.nda
     return out.reshape(logits_f32.shape[:-1])
 
 
+def mask_top_k(logits_f32: np.ndarray, top_k: int) -> np.ndarray:
+    """Copy of logits with every entry outside its row's top_k set to -inf
+    (top-k truncation of a sampler; ties at the cut keep the lower ids)."""
+    flat = logits_f32.reshape(-1, logits_f32.shape[-1])
+    out = np.full_like(flat, -np.inf)
+    if top_k > 0:
+        keep = np.argsort(-flat, axis=-1, kind="stable")[:, :top_k]
+        rows = np.arange(flat.shape[0])[:, None]
+        out[rows, keep] = flat[rows, keep]
+    return out.reshape(logits_f32.shape)
+
+
 def rejection_workload(B, K, V, sigma=2.0, noise_sigma=0.5, temperature=1.0, seed=0,
-                       dtype="bf16"):
+                       dtype="bf16", top_k=None):
     """target [B, K+1, V] = round(N(0, sigma)); draft logits [B, K, V] =
-    round(target + N(0, noise_sigma)); draft ids x ~ softmax(draft/T) (a
-    separate PCG64 stream); uniforms [B, K+1] from Philox."""
+    round(target + N(0, noise_sigma)); with top_k, each row of both keeps
+    only its top_k entries and the rest are -inf; draft ids x ~
+    softmax(draft/T) (a separate PCG64 stream); uniforms [B, K+1] from
+    Philox."""
     rng = _rng(seed)
     tgt32 = rng.standard_normal((B, K + 1, V), dtype=np.float32)
     if sigma != 1.0:
@@ -158,6 +172,15 @@ def rejection_workload(B, K, V, sigma=2.0, noise_sigma=0.5, temperature=1.0, see
         draft_logits = (tgt32[:, :K, :] + noise).astype(np.float32)
         dwide = draft_logits
     del noise
+    if top_k is not None:
+        tw = bf16_bits_to_f32(target) if dtype == "bf16" else target
+        target = mask_top_k(tw, top_k)
+        dwide = mask_top_k(dwide, top_k)
+        if dtype == "bf16":
+            target = f32_to_bf16_bits(target)
+            draft_logits = f32_to_bf16_bits(dwide)
+        else:
+            draft_logits = dwide
     xs = gumbel_max_sample(dwide, temperature, _rng(seed + 7919)).astype(np.int32) if K > 0 \
         else np.zeros((B, 0), np.int32)
     u = philox_uniforms((B, K + 1), seed)

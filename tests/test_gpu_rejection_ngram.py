@@ -59,6 +59,20 @@ def test_rejection_small_shapes_temperatures(orc, T):
     assert total_mism <= total_flag
 
 
+@pytest.mark.parametrize("dtype,T,top_k", [("bf16", 1.0, 50), ("f32", 0.7, 4000), ("bf16", 1.3, 1)])
+def test_rejection_masked_logits(orc, dtype, T, top_k):
+    """Top-k truncated rows: every entry outside a row's top_k is -inf in
+    the target and draft logits (the two keep different sets, so drafts can
+    have p = 0).  Masked entries carry probability 0 on both sides."""
+    wl = W.rejection_workload(24, 4, 50000, 2.0, 0.7, T, seed=4242 + top_k, dtype=dtype, top_k=top_k)
+    _rej_case(orc, wl, label="masked top%d %s T%.1f" % (top_k, dtype, T))
+    sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 2048)
+    try:
+        _rej_case(orc, wl, label="masked top%d %s T%.1f split" % (top_k, dtype, T))
+    finally:
+        sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 0)
+
+
 def test_rejection_split_rows_and_repeat(orc):
     sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 2048)
     try:

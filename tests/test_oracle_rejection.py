@@ -190,3 +190,32 @@ def test_flags_and_draft_len(orc):
     u2 = np.array([[np.nextafter(np.float32(ratio), np.float32(0)), 0.5]], np.float32)
     out2 = orc.verify_rejection(tl2, dl2, np.array([[0]], np.int32), u2)
     assert out2["accept_tie"][0]
+
+
+def test_masked_entries_equal_smaller_vocabulary(orc):
+    """A -inf logit has probability 0, so a row with masked entries is the
+    same distribution as the row with those entries removed: embedding a
+    V'-token problem into V > V' ids (kept ids increasing, the rest -inf in
+    both target and draft) must give the same decisions, the same p and q,
+    and the same emitted tokens mapped through the embedding."""
+    rng = np.random.default_rng(77)
+    B, K, Vs, V = 24, 4, 40, 300
+    for T in (1.0, 0.7):
+        tl = (2.0 * rng.standard_normal((B, K + 1, Vs))).astype(np.float32)
+        dl = (tl[:, :K] + 0.5 * rng.standard_normal((B, K, Vs))).astype(np.float32)
+        x = rng.integers(0, Vs, size=(B, K)).astype(np.int32)
+        u = rng.random((B, K + 1), dtype=np.float32)
+        ids = np.sort(rng.choice(V, size=Vs, replace=False)).astype(np.int32)
+        tL = np.full((B, K + 1, V), -np.inf, np.float32)
+        dL = np.full((B, K, V), -np.inf, np.float32)
+        tL[..., ids] = tl
+        dL[..., ids] = dl
+        small = orc.verify_rejection(tl, dl, x, u, T)
+        large = orc.verify_rejection(tL, dL, ids[x], u, T)
+        np.testing.assert_array_equal(large["accepted"], small["accepted"])
+        np.testing.assert_array_equal(large["p_draft"], small["p_draft"])
+        np.testing.assert_array_equal(large["q_draft"], small["q_draft"])
+        for b in range(B):
+            n = small["accepted"][b]
+            np.testing.assert_array_equal(large["emitted"][b, :n + 1], ids[small["emitted"][b, :n + 1]])
+            assert (large["emitted"][b, n + 1:] == -1).all()
