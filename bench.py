@@ -33,6 +33,13 @@ sys.path.insert(0, ROOT)
 METRIC = "verified positions/s + HBM GB/s (% of peak) at V=128k; n-gram proposals/s"
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+# What one timed launch of each call runs, in stream order.
+LAUNCH_KERNELS = {
+    "greedy": "sv_verify_greedy: k_row_argmax<bf16> (2304 rows) + k_greedy_scan",
+    "tree": "sv_verify_tree: k_row_argmax<bf16> (2048 rows) + k_tree_scan",
+    "rejection": "sv_verify_rejection: k_rej_stats + k_rej_scan + k_rej_chunks + k_rej_select",
+}
+
 KERNEL_SOURCES = {
     "greedy": ["proposal_sv_verify_amd/csrc/argmax_verify.hip",
                "proposal_sv_verify_amd/csrc/sv_device.hpp",
@@ -113,10 +120,10 @@ def run_gpu(args, ng, rj, gr, tr):
             e[j + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {name: float(np.mean([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)])) * 1e3
-           for j, (name, _) in enumerate(calls)}
+    samples = {name: np.array([ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)]) * 1e3
+               for j, (name, _) in enumerate(calls)}
     outs = {name: {k: v.cpu().numpy() for k, v in c.out.items()} for name, c in calls}
-    return wall, per, outs, d
+    return wall, samples, outs, d
 
 
 def ngram_bandwidth_mode(args):
@@ -212,6 +219,19 @@ def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
                 sample="%d full step(s): all four calls over every sequence (%.1f s)" % (n, el)), parity
 
 
+def calibrate_copy():
+    """A plain device copy of 256 MiB (reads 256 MiB, writes 256 MiB), three
+    times: the reference launch for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def load_traffic(name, per_launch_us_unused=None):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if the
     kernel's sources are unchanged since they were taken."""
@@ -234,6 +254,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-bandwidth-mode", action="store_true",
                     help="skip the 16384-context n-gram measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the steps, copy a 256 MiB device buffer three times (a "
+                         "kernel of known traffic for scaling the rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -241,7 +264,10 @@ def main():
         sys.exit(2)
 
     ng, rj, gr, tr = make_inputs()
-    wall, per, outs, _ = run_gpu(args, ng, rj, gr, tr)
+    wall, samples, outs, _ = run_gpu(args, ng, rj, gr, tr)
+    per = {name: float(np.mean(v)) for name, v in samples.items()}
+    if args.calibrate_copy:
+        calibrate_copy()
     K = args.steps
     ms_step = wall / K * 1e3
     positions = 64 * 6 + 256 * 9 + 32 * 64
@@ -256,7 +282,11 @@ def main():
     kernels = {}
     for name, us in per.items():
         gbs = algo[name] / us / 1e3
-        kernels[name] = dict(us_per_call=round(us, 2), algorithmic_bytes=algo[name],
+        p10, p50, p90 = np.percentile(samples[name], [10, 50, 90])
+        kernels[name] = dict(us_per_call=round(us, 2), us_p10_p50_p90=[round(float(p10), 2),
+                                                                     round(float(p50), 2),
+                                                                     round(float(p90), 2)],
+                             algorithmic_bytes=algo[name],
                              gb_per_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4),
                              units_per_s=round(units[name] / us * 1e6, 1),
                              unit="proposals" if name == "ngram" else "positions")
@@ -265,8 +295,8 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4),
                     traffic=load_traffic(dom) if dom in KERNEL_SOURCES else None,
-                    kernel=dom, algorithmic_bytes_per_launch=algo[dom],
-                    avg_launch_us=round(per[dom], 2))
+                    kernel=dom, launch=LAUNCH_KERNELS[dom],
+                    algorithmic_bytes_per_launch=algo[dom], avg_launch_us=round(per[dom], 2))
 
     result = dict(metric=METRIC, value=round(positions * K / wall, 1), unit="verified positions/s",
                   n_gpus=1, steps=K, warmup=args.warmup, ms_per_step=round(ms_step, 4),

@@ -48,7 +48,8 @@
  *    Calls that share a workspace must be ordered on one stream; calls
  *    running concurrently need their own.
  *  - argmax ties resolve to the LOWEST token id (the numpy / torch rule);
- *    -0.0 and +0.0 compare equal.  Rows must be free of NaN.
+ *    -0.0 and +0.0 compare equal.  -inf entries are allowed (a masked
+ *    vocabulary); NaN and +inf are not.
  *  - The device must be gfx950 (else SV_ERR_UNSUPPORTED).
  */
 #ifndef SPECVERIFY_H
@@ -101,8 +102,11 @@ const char *sv_last_error_message(void);
  * thread-safe; a value <= 0 restores the default).  Rows are cut into
  * segments so that a call launches about SV_TUNE_TARGET_WORKGROUPS
  * workgroups (default 2048: eight per compute unit) without segments
- * shorter than SV_TUNE_MIN_SEGMENT_BYTES (default 32768).  Workspace sizes
- * follow the current setting: query them after changing it.
+ * shorter than SV_TUNE_MIN_SEGMENT_BYTES (default 32768).  The rejection
+ * statistics kernel works per wave: about 4 * SV_TUNE_TARGET_WORKGROUPS
+ * pieces, at most 16 per row, none shorter than a quarter of
+ * SV_TUNE_MIN_SEGMENT_BYTES.  Workspace sizes follow the current setting:
+ * query them after changing it.
  */
 #define SV_TUNE_TARGET_WORKGROUPS 1
 #define SV_TUNE_MIN_SEGMENT_BYTES 2
@@ -162,7 +166,8 @@ int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
  *   flags, stats as for sv_verify_greedy.
  * Arithmetic: exp in fp32 per element, every sum, normaliser, ratio and CDF
  * in fp64; p_i(x_i), q_i(x_i) use fp64 exp.  Decisions agree with an fp64
- * evaluation except within a rounding band of a tie.
+ * evaluation except within a rounding band of a tie.  A -inf logit has
+ * probability 0; every row needs at least one finite logit.
  * Limits: 1 <= B, 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= SV_MAX_V.
  */
 size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V);
