@@ -8,13 +8,20 @@
 // at the start of the context.  The method's answer is the largest n with
 // some m(e) >= n (n >= n_min), and for that n the largest such e -- i.e. the
 // maximum of the key (min(m(e), n_max) << 26) | e over all e with
-// m(e) >= n_min.  One workgroup per context scans 1024-position tiles from
-// the end of the context backwards: the tile goes to LDS with the 32
-// positions below it (the halo, which the prefetched next tile supplies),
-// every thread scores four consecutive candidates against the suffix held
-// in LDS, a workgroup max combines the keys, and the scan stops as soon as
-// a full-length (n_max) match is known, since nothing further back can beat
-// it.
+// m(e) >= n_min.
+//
+// kW waves work on one context (kW = 1 for many contexts, so that each
+// wave's in-flight reads are few at its early exit; kW = 4 for few, so that
+// a context is scanned four tiles at a time).  Wave `sub` scores the
+// 256-position tiles t_top - sub, t_top - sub - kW, ... from the end of the
+// context backwards; each tile comes with the 32 positions below it (the
+// longest comparison's reach), through a ring of kDepth loads per lane, so
+// kDepth - 1 tiles are in flight while one is scored.  A lane holds four
+// consecutive candidate ends and tests their last token against the
+// suffix's last token in registers; only the rare hits compare further,
+// from the tile staged in the wave's LDS.  A wave stops once a full-length
+// (n_max) match is known at or above its next tile, since nothing further
+// back can beat it; the keys' maximum is the answer.
 
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
@@ -22,103 +29,177 @@
 namespace sv {
 namespace {
 
-constexpr int kTile = 4 * kThreads;   // candidate end positions per tile
-constexpr int kHalo = 32;             // positions kept below a tile (>= SV_MAX_NGRAM)
+constexpr int kTile = 4 * 64;         // candidate end positions per tile (one wave, 4 per lane)
+constexpr int kHalo = 32;             // positions staged below a tile (> the longest comparison)
+constexpr int kDepth = 4;             // tiles per lane in the load ring
 constexpr int kEndBits = 26;          // key = (match length << 26) | end position
-static_assert(SV_MAX_NGRAM < kHalo + 1, "halo must cover the longest lookup");
+static_assert(SV_MAX_NGRAM < kHalo + 1, "the halo must cover the longest comparison");
 static_assert((1 << kEndBits) >= SV_MAX_CONTEXT, "end positions must fit the key");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Four tokens at positions pos .. pos+3 (pos % 4 == 0); positions >= L read 0.
-__device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int L, bool vec_ok)
+// Four tokens at positions pos .. pos+3 of a context row of `stride` ints
+// (pos % 4 == 0), loaded unconditionally: positions outside the row are
+// clamped into it, and the caller never uses them.  kVec: the row is
+// 16-byte aligned and stride % 4 == 0.
+template <bool kVec>
+__device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int stride)
 {
-    if (vec_ok && pos + 3 < L)
-        return __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(c + pos));
-    i32x4 r = {0, 0, 0, 0};
-    if (pos < L)
-        r.x = c[pos];
-    if (pos + 1 < L)
-        r.y = c[pos + 1];
-    if (pos + 2 < L)
-        r.z = c[pos + 2];
-    if (pos + 3 < L)
-        r.w = c[pos + 3];
-    return r;
+    if constexpr (kVec) {
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const i32x4 *>(c + max(0, min(pos, stride - 4))));
+    } else {
+        const int last = stride - 1;
+        i32x4 r;
+        r.x = c[max(0, min(pos, last))];
+        r.y = c[max(0, min(pos + 1, last))];
+        r.z = c[max(0, min(pos + 2, last))];
+        r.w = c[max(0, min(pos + 3, last))];
+        return r;
+    }
 }
 
+template <bool kVec, int kW>
 __global__ __launch_bounds__(kThreads) void k_ngram(const NgramParams p)
 {
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int32_t *c = p.tokens + static_cast<int64_t>(b) * p.ctx_stride;
-    const bool vec_ok = p.vec_ok != 0;
+    static_assert(kWaves % kW == 0, "whole contexts per workgroup");
+    __shared__ int s_buf[kWaves][kHalo + kTile];  // a wave's tile, halo below it
+    __shared__ int s_suf[kWaves][64];             // s_suf[j] = c[L-1-j] for j < n_max
+    __shared__ int s_full[kWaves / kW];           // highest tile with a full-length match
+    __shared__ int s_key[kWaves];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int sub = w % kW;
+    const int slot = w / kW;
+    const int b = blockIdx.x * (kWaves / kW) + slot;
+    const bool live = b < p.B;                    // uniform over the context's waves
+    const int stride = static_cast<int>(p.ctx_stride);
+    const int32_t *c = p.tokens + static_cast<int64_t>(live ? b : 0) * p.ctx_stride;
+    int *buf = s_buf[w];
+    int *sfx = s_suf[w];
     unsigned fl = 0;
-    int L = p.lengths[b];
-    if (L < 0 || static_cast<int64_t>(L) > p.ctx_stride) {
+    int L = live ? p.lengths[b] : 0;
+    if (L < 0 || L > stride) {
         fl |= SV_FLAG_BAD_LEN;
         L = 0;
     }
     const int nmax = p.n_max, nmin = p.n_min;
+    if (kW > 1) {
+        if (threadIdx.x < kWaves / kW)
+            s_full[threadIdx.x] = -1;
+        __syncthreads();
+    }
 
-    __shared__ int s_suf[kHalo];                 // s_suf[j] = c[L-1-j]
-    __shared__ int s_buf[kHalo + kTile];         // positions [lo - kHalo, lo + kTile)
-    if (tid < nmax && tid < L)
-        s_suf[tid] = c[L - 1 - tid];
-
-    int best = 0;                                // best key so far; 0 = no match
-    const int e_hi = L - 2;                      // most recent candidate end
-    const int e_lo = nmin - 1;                   // earliest end holding n_min tokens
-    if (e_hi >= e_lo) {
+    int best = 0;                                 // this lane's best key; 0 = no match
+    const int e_hi = L - 2;                       // most recent candidate end
+    const int e_lo = nmin - 1;                    // earliest end holding n_min tokens
+    if (live && e_hi >= e_lo) {
         const int t_top = e_hi / kTile, t_bot = e_lo / kTile;
-        i32x4 cur = load4(c, t_top * kTile + 4 * tid, L, vec_ok);
-        i32x4 nxt = {0, 0, 0, 0};
-        if (t_top > 0)
-            nxt = load4(c, (t_top - 1) * kTile + 4 * tid, L, vec_ok);
-        for (int t = t_top; t >= t_bot; --t) {
-            const int lo = t * kTile;
-            s_buf[kHalo + 4 * tid + 0] = cur.x;
-            s_buf[kHalo + 4 * tid + 1] = cur.y;
-            s_buf[kHalo + 4 * tid + 2] = cur.z;
-            s_buf[kHalo + 4 * tid + 3] = cur.w;
-            if (t > 0 && tid >= kThreads - kHalo / 4) {   // the halo: top of tile t-1
-                const int h = 4 * (tid - (kThreads - kHalo / 4));
-                s_buf[h + 0] = nxt.x;
-                s_buf[h + 1] = nxt.y;
-                s_buf[h + 2] = nxt.z;
-                s_buf[h + 3] = nxt.w;
-            }
-            __syncthreads();
-            cur = nxt;
-            if (t - 2 >= 0 && t - 1 >= t_bot)    // prefetch tile t-2 (halo or scan)
-                nxt = load4(c, (t - 2) * kTile + 4 * tid, L, vec_ok);
-
-            int key = 0;
+        // the suffix loads go first, so waiting for them drains nothing else
+        const int suf = c[max(0, L - 1 - min(lane, nmax - 1))];
+        const int s0 = c[L - 1];
+        __builtin_amdgcn_sched_barrier(0);
+        // ring slot u holds the i-th tile of this wave, i = u + kDepth * r;
+        // lanes 0..7 also fetch the halo (the 32 positions below the tile)
+        auto tile_of = [&](int i) { return t_top - sub - kW * i; };
+        auto fetch = [&](int i, i32x4 &v, i32x4 &h) {
+            const int t = max(tile_of(i), t_bot);
+            v = load4<kVec>(c, t * kTile + 4 * lane, stride);
+            h = load4<kVec>(c, t * kTile - kHalo + 4 * (lane & 7), stride);
+        };
+        i32x4 q[kDepth], hq[kDepth];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int e = lo + 4 * tid + k;
-                if (e < e_lo || e > e_hi)
-                    continue;
-                int m = 0;
-                while (m < nmax && e - m >= 0 && s_buf[kHalo + (e - lo) - m] == s_suf[m])
-                    ++m;
-                if (m >= nmin)
-                    key = max(key, (m << kEndBits) | e);
+        for (int u = 0; u < kDepth; ++u)
+            fetch(u, q[u], hq[u]);
+        sfx[lane] = suf;                          // entries past n_max - 1 are not read
+        // Every ring load is issued whether or not its step still scores a
+        // tile (the scan ends only at the end of a round): with the same loads
+        // on every path, the compiler's wait counts stay exact.  Past the
+        // bottom they re-read the last tile.
+        bool stop = false;
+        for (int r = 0;; r += kDepth) {
+#pragma unroll
+            for (int u = 0; u < kDepth; ++u) {
+                const int i = r + u;
+                const int t = tile_of(i);
+                int full = -1;
+                if (kW > 1)
+                    full = s_full[slot];
+                const bool active = !stop && t >= t_bot && full < t;   // uniform over the wave
+                const i32x4 v = q[u];
+                if (active) {
+                    buf[kHalo + 4 * lane + 0] = v.x;
+                    buf[kHalo + 4 * lane + 1] = v.y;
+                    buf[kHalo + 4 * lane + 2] = v.z;
+                    buf[kHalo + 4 * lane + 3] = v.w;
+                    if (lane < 8) {
+                        const i32x4 h = hq[u];
+                        buf[4 * lane + 0] = h.x;
+                        buf[4 * lane + 1] = h.y;
+                        buf[4 * lane + 2] = h.z;
+                        buf[4 * lane + 3] = h.w;
+                    }
+                }
+                fetch(active ? i + kDepth : i, q[u], hq[u]);
+                if (active) {
+                    const int lo = t * kTile;
+                    const int tok[4] = {v.x, v.y, v.z, v.w};
+                    unsigned hit = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = lo + 4 * lane + k;
+                        if (tok[k] == s0 && e >= e_lo && e <= e_hi)
+                            hit |= 1u << k;
+                    }
+                    if (__ballot(hit != 0)) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            if (hit & (1u << k)) {
+                                const int e = lo + 4 * lane + k;
+                                int m = 1;
+                                while (m < nmax && e - m >= 0 &&
+                                       buf[kHalo + 4 * lane + k - m] == sfx[m])
+                                    ++m;
+                                if (m >= nmin)
+                                    best = max(best, (m << kEndBits) | e);
+                            }
+                        }
+                    }
+                    if (__ballot((best >> kEndBits) == nmax)) {
+                        stop = true;
+                        if (kW > 1 && lane == 0)
+                            atomicMax(&s_full[slot], t);
+                    }
+                } else {
+                    stop = true;
+                }
             }
-            key = block_max_int(key);
-            if ((key >> kEndBits) > (best >> kEndBits))
-                best = key;                      // longer match; ties keep the later end
-            if ((best >> kEndBits) == nmax)
-                break;                           // uniform: every thread holds `best`
+            if (stop)
+                break;
         }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            best = max(best, __shfl_xor(best, off, 64));
+    }
+    if (kW > 1) {
+        if (lane == 0)
+            s_key[w] = best;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kW; ++k)
+            best = max(best, s_key[slot * kW + k]);
+        if (sub != 0 || !live)
+            return;
+    } else if (!live) {
+        return;
     }
 
     const int n = best >> kEndBits;
     const int e = best & ((1 << kEndBits) - 1);
     const int m = n > 0 ? min(p.K, L - 1 - e) : 0;
-    for (int k = tid; k < p.K; k += kThreads)
+    for (int k = lane; k < p.K; k += 64)
         p.proposal[static_cast<int64_t>(b) * p.K + k] = k < m ? c[e + 1 + k] : -1;
-    if (tid == 0) {
+    if (lane == 0) {
         p.proposal_len[b] = m;
         if (p.match_n)
             p.match_n[b] = n;
@@ -129,12 +210,25 @@ __global__ __launch_bounds__(kThreads) void k_ngram(const NgramParams p)
     }
 }
 
+template <bool kVec, int kW>
+hipError_t launch_w(const NgramParams &p, hipStream_t s)
+{
+    constexpr int kPerWg = kWaves / kW;
+    hipLaunchKernelGGL((k_ngram<kVec, kW>), dim3(static_cast<unsigned>((p.B + kPerWg - 1) / kPerWg)),
+                       dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 } // namespace
 
 hipError_t launch_ngram(const NgramParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_ngram, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    // one wave per context once the contexts alone fill the chip's wave slots
+    // (256 CUs x 32) twice; four waves per context below that
+    const bool many = p.B >= 2 * 256 * 32;
+    if (p.vec_ok)
+        return many ? launch_w<true, 1>(p, s) : launch_w<true, 4>(p, s);
+    return many ? launch_w<false, 1>(p, s) : launch_w<false, 4>(p, s);
 }
 
 } // namespace sv
