@@ -31,7 +31,8 @@ namespace {
 
 constexpr int kTile = 4 * 64;         // candidate end positions per tile (one wave, 4 per lane)
 constexpr int kHalo = 32;             // positions staged below a tile (> the longest comparison)
-constexpr int kDepth = 4;             // tiles per lane in the load ring
+constexpr int kDepth = 2;             // tiles per lane in the load ring (measured best: deeper
+                                      // rings fetch more past each early exit)
 constexpr int kEndBits = 26;          // key = (match length << 26) | end position
 static_assert(SV_MAX_NGRAM < kHalo + 1, "the halo must cover the longest comparison");
 static_assert((1 << kEndBits) >= SV_MAX_CONTEXT, "end positions must fit the key");
@@ -60,7 +61,7 @@ __device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int stride)
 }
 
 template <bool kVec, int kW>
-__global__ __launch_bounds__(kThreads) void k_ngram(const NgramParams p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_ngram(const NgramParams p)
 {
     static_assert(kWaves % kW == 0, "whole contexts per workgroup");
     __shared__ int s_buf[kWaves][kHalo + kTile];  // a wave's tile, halo below it
