@@ -5,12 +5,13 @@
 // Kernel 1 (row statistics).  One wave per (row, piece) over the K+1
 // target rows and K draft rows of every sequence streams the logits once
 // with 16-byte loads (the pieces are sized so that every wave of the launch
-// is resident at once).  Each lane sums exp((l - ref) / T) against its own
-// reference, set by its first vector and moved only when a vector's terms
-// leave a wide fp32 range (the fp64 rescale almost never runs); the exp is
-// the compensated hardware exp2 (about one ulp), 8-element partial sums are
-// fp32, running sums fp64.  The wave combines its lanes onto their largest
-// reference and writes (reference, sum).
+// is resident at once).  Each lane sums exp(l / T) against the fixed
+// reference 0 with the compensated hardware exp2 (about one ulp): fp32 sums
+// of 8 terms, fp64 across them.  The rare vectors whose fp32 sum leaves a
+// wide range (logits above about 44 T, -inf entries, rows far below 0) go
+// through a careful path with its own reference and fp64 rescales.  The
+// wave combines its lanes onto their largest reference and writes
+// (reference, sum).
 //
 // Kernel 2 (accept scan).  One workgroup per sequence: merge the segment
 // statistics of each row in LDS, then one lane per draft position computes
@@ -44,10 +45,14 @@ static_assert(kChunkPerThread * kThreads == kRejChunk, "chunk must split evenly 
 static_assert(kSubPerChunk == kWaves, "one sub-chunk per wave");
 static_assert(kSubPerThread * kThreads == kRejSub, "sub-chunk must split evenly over the threads");
 
-// The reference of a thread's sum moves when the fp32 sum of one vector's
-// terms leaves [0, kBig] (a term above about e^44, or NaN from a -inf
-// logit): e^44 keeps every fp32 sum far from overflow.
+// A lane's fast path sums e^(l/T) against the fixed reference 0 -- no
+// subtraction per element -- in fp32 per vector of 8 and fp64 across
+// vectors.  A vector whose fp32 sum leaves [kTiny, kBig] (a term above
+// about e^44, NaN from a -inf logit, or every term below about e^-41 while
+// nothing larger has been seen) goes through the careful path, which keeps
+// a second sum against the lane's own reference.
 constexpr float kBig = 18446744073709551616.0f;   // 2^64
+constexpr float kTiny = 8.67361737988403547e-19f; // 2^-60
 
 // z * exp((m - M) / T) in fp64: moves a sum z taken against the reference m
 // onto the reference M (z == 0: nothing was summed).  Out of line: it runs
@@ -63,35 +68,54 @@ __device__ __forceinline__ double rescale(double z, float m, float M, double inv
     return z != 0.0 ? rescale_slow(z, m, M, inv_t_d) : 0.0;
 }
 
-// Sum of e^((l - ref) / T) over n values, moving (ref, z) first when a value
-// exceeds ref; -inf values add 0.  The careful path of the statistics loop.
+// A lane's two running sums: z0 = sum of e^(l/T) (reference 0) and zc =
+// sum of e^((l - rc)/T) over the vectors the careful path could not add to
+// z0 (rc = -inf while there are none).
+struct LaneSums {
+    double z0 = 0.0;
+    double zc = 0.0;
+    float rc = -__builtin_inff();
+};
+
+// The careful path for n values whose fast fp32 sum `s` is out of range.
 template <bool kUnitT, int n>
-__device__ __forceinline__ float careful_sum(const float (&f)[n], float &ref, double &z, float inv_t, double inv_t_d)
+__device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSums &ls, float inv_t,
+                                            double inv_t_d)
 {
+    // -inf values made the sum NaN: the same sum with -inf read as 0
+    if (!(s == s)) {
+        s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < n; ++j)
+            s += exp_cz(kUnitT ? f[j] : f[j] * inv_t);
+    }
+    // in range, or too small to matter next to what z0 already holds
+    if ((s >= kTiny || (s >= 0.0f && ls.z0 >= 1.0)) && s <= kBig) {
+        ls.z0 += static_cast<double>(s);
+        return;
+    }
     float vm = f[0];
 #pragma unroll
     for (int j = 1; j < n; ++j)
         vm = fmaxf(vm, f[j]);
-    if (vm > ref) {
-        z = rescale(z, ref, vm, inv_t_d);
-        ref = vm;
-    }
-    float s = 0.0f;
-    if (ref != -__builtin_inff()) {
+    if (vm == -__builtin_inff())
+        return;
+    float t = 0.0f;
 #pragma unroll
-        for (int j = 0; j < n; ++j)
-            s += exp_cz(kUnitT ? f[j] - ref : (f[j] - ref) * inv_t);
+    for (int j = 0; j < n; ++j)
+        t += exp_cz(kUnitT ? f[j] - vm : (f[j] - vm) * inv_t);
+    if (vm > ls.rc) {
+        ls.zc = rescale(ls.zc, ls.rc, vm, inv_t_d) + static_cast<double>(t);
+        ls.rc = vm;
+    } else {
+        ls.zc += rescale(static_cast<double>(t), vm, ls.rc, inv_t_d);
     }
-    return s;
 }
 
 // One wave per work item (row, piece); a workgroup carries four items.
-// Each lane sums e^((l - ref) / T) against its own reference, which starts
-// at -inf (so its first vector takes the careful path and sets it) and
-// moves only through the careful path; the fast path is the compensated
-// exp and an fp32 sum per vector, accumulated in fp64.  The reference need
-// not be the true maximum: any value within e^44 of it keeps the sums exact
-// to fp32 rounding, and the row merge accepts any reference.
+// The partial's reference is the largest of 0 and the lanes' careful
+// references, so every element of the piece is at most about e^44 above it
+// (fast-path vectors sum to at most 2^64 against 0).
 template <typename E, bool kUnitT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_stats(const RejectParams p)
 {
@@ -111,8 +135,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     const int i = is_target ? r : r - (K + 1);
     const bool needed = is_target ? i <= len : i < len;
 
-    float ref = -__builtin_inff();
-    double z = 0.0;
+    LaneSums ls;
     if (needed) {
         const E *rp = is_target
                           ? static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + i) * p.row_stride
@@ -121,7 +144,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const int hi = min(p.V, lo + p.seg_len);
         const float inv_t = p.inv_t;
         const double inv_t_d = p.inv_t_d;
-        auto arg = [&](float x) { return kUnitT ? x - ref : (x - ref) * inv_t; };
+        auto arg = [&](float x) { return kUnitT ? x : x * inv_t; };
         stream_segment<E, 4, 64>(
             rp, lo, hi, lane,
             [&](const float(&f)[Elem<E>::kPerVec], int) {
@@ -130,23 +153,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 #pragma unroll
                 for (int j = 1; j < PV; ++j)
                     s += exp_c(arg(f[j]));
-                if (!(s <= kBig))
-                    s = careful_sum<kUnitT>(f, ref, z, inv_t, inv_t_d);
-                z += static_cast<double>(s);
+                if (s >= kTiny && s <= kBig)
+                    ls.z0 += static_cast<double>(s);
+                else
+                    careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
             },
             [&](float x, int) {
-                float s = exp_c(arg(x));
-                if (!(s <= kBig)) {
+                const float s = exp_c(arg(x));
+                if (s >= kTiny && s <= kBig) {
+                    ls.z0 += static_cast<double>(s);
+                } else {
                     const float f[1] = {x};
-                    s = careful_sum<kUnitT>(f, ref, z, inv_t, inv_t_d);
+                    careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
                 }
-                z += static_cast<double>(s);
             });
     }
-    // onto the item's largest reference: one fp64 rescale per lane (none for
-    // the lane holding it), then a wave sum
-    const float M = wave_max(ref);
-    const double zz = wave_sum(ref == M ? z : rescale(z, ref, M, p.inv_t_d));
+    // the lane's sums onto R = max(0, rc), then the wave's onto their largest R
+    const float R = fmaxf(0.0f, ls.rc);
+    const double zl = (R == 0.0f ? ls.z0 : rescale(ls.z0, 0.0f, R, p.inv_t_d)) +
+                      (ls.rc == R ? ls.zc : rescale(ls.zc, ls.rc, R, p.inv_t_d));
+    const float M = wave_max(R);
+    const double zz = wave_sum(R == M ? zl : rescale(zl, R, M, p.inv_t_d));
     if (lane == 0)
         p.partial[item] = SoftPartial{zz, M, 0};
 }
