@@ -113,9 +113,10 @@ __device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSu
 }
 
 // One wave per work item (row, piece); a workgroup carries four items.
-// The partial's reference is the largest of 0 and the lanes' careful
-// references, so every element of the piece is at most about e^44 above it
-// (fast-path vectors sum to at most 2^64 against 0).
+// The partial's reference is at most about e^44 below every element of the
+// piece (fast-path vectors sum to at most 2^64 against 0; careful vectors
+// are taken against their own maximum) and, when the piece has terms of
+// non-negligible size against 0, at least 0.
 template <typename E, bool kUnitT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_stats(const RejectParams p)
 {
@@ -168,8 +169,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
                 }
             });
     }
-    // the lane's sums onto R = max(0, rc), then the wave's onto their largest R
-    const float R = fmaxf(0.0f, ls.rc);
+    // the lane's sums onto its reference R, then the wave's onto their
+    // largest R.  With terms summed against 0, R = max(0, rc): those terms
+    // put the lane's maximum within about e^42 of 0.  Without any (a lane
+    // whose values all lie far below 0), R = rc, so that the sampling
+    // kernels' fp32 exp against the row's reference stays clear of
+    // underflow.
+    const float R = ls.z0 != 0.0 ? fmaxf(0.0f, ls.rc) : ls.rc;
     const double zl = (R == 0.0f ? ls.z0 : rescale(ls.z0, 0.0f, R, p.inv_t_d)) +
                       (ls.rc == R ? ls.zc : rescale(ls.zc, ls.rc, R, p.inv_t_d));
     const float M = wave_max(R);

@@ -73,6 +73,32 @@ def test_rejection_masked_logits(orc, dtype, T, top_k):
         sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 0)
 
 
+@pytest.mark.parametrize("case", ["shift+60", "shift-90", "outlier+70", "shift+20_T0.3"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rejection_extreme_logits(orc, case, dtype):
+    """Logits far from 0: every row shifted up (terms above e^44 against a
+    zero reference), shifted down (terms below e^-41), one large outlier
+    per row, and a low temperature.  Softmax is shift-invariant, so the
+    drafts sampled before the shift keep their distribution."""
+    T = 0.3 if "T0.3" in case else 1.0
+    seed = {"shift+60": 61, "shift-90": 62, "outlier+70": 63, "shift+20_T0.3": 64}[case]
+    wl = W.rejection_workload(12, 3, 5000, 2.0, 0.5, T, seed=seed, dtype=dtype)
+    widen = W.bf16_bits_to_f32 if dtype == "bf16" else (lambda a: a)
+    narrow = W.f32_to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    t32, d32 = widen(wl["target"]).copy(), widen(wl["draft_logits"]).copy()
+    if case.startswith("shift"):
+        off = np.float32(float(case.split("_")[0][5:]))
+        t32 += off
+        d32 += off
+    else:
+        rng = np.random.default_rng(5)
+        for a in (t32, d32):
+            flat = a.reshape(-1, a.shape[-1])
+            flat[np.arange(flat.shape[0]), rng.integers(0, flat.shape[1], flat.shape[0])] = 70.0
+    wl = dict(wl, target=narrow(t32), draft_logits=narrow(d32))
+    _rej_case(orc, wl, label="extreme %s %s" % (case, dtype))
+
+
 def test_rejection_split_rows_and_repeat(orc):
     sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 2048)
     try:
