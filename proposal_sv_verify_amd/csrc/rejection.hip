@@ -17,7 +17,9 @@
 // statistics of each row in LDS, then one lane per draft position computes
 // p_k(x_k) and q_k(x_k) with fp64 exp and the test u_k < p/q in fp64; a
 // ballot of the rejections gives the first one, n.  The lane at position n
-// publishes the statistics of row pair n.
+// publishes the statistics of row pair n.  (Running this inside kernel 3's
+// workgroups instead was measured slower: every chunk then waits out the
+// whole decision before loading its data.)
 //
 // Kernel 3 (final-sample masses).  The final token is drawn from one row
 // pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
@@ -190,49 +192,77 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // inside a branch or loop is waited for on the spot, and each such wait costs
 // a full memory round trip.
 
-// Kernel 2: one workgroup per sequence, draft positions in blocks of 64.
-// A block needs the statistics of 64 target rows and 64 draft rows: their
+// The accept decision of one sequence (steps a4 and the choice of row pair
+// for a5), run by a whole workgroup: draft positions in blocks of 64.  A
+// block needs the statistics of its target rows and draft rows: their
 // segment partials are staged in LDS, each row's maximum is found, every
 // partial is moved onto it (the fp64 rescales run in parallel, one thread per
 // partial) and the row sums are formed; then wave 0 runs the accept test with
-// one lane per position.
-constexpr int kScanRows = 128;
+// one lane per position.  In LDS, target row base + i sits at slot i and
+// draft row base + i at slot D0 + i, D0 = min(64, K + 1): for K < 64 the rows
+// are packed (2K + 1 of them).  With `publish` the workgroup also writes the
+// call's per-sequence outputs and the sequence state; every thread gets the
+// state back.
+constexpr int kScanRows = 128;                                 // LDS row slots, at most
 constexpr int kScanPer = kScanRows * kMaxSegs / kThreads;      // partials per thread, at most
 
-template <typename E>
-__global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
+__host__ __device__ constexpr int scan_rows(int K) { return (K + 1 < 64 ? K + 1 : 64) + (K < 64 ? K : 64); }
+
+__host__ __device__ constexpr size_t scan_lds_bytes(int K, int segs)
 {
-    __shared__ float s_m[kScanRows * kMaxSegs];
-    __shared__ double s_z[kScanRows * kMaxSegs];
-    __shared__ float s_M[kScanRows];
-    __shared__ double s_Z[kScanRows];
-    const int b = blockIdx.x;
+    return static_cast<size_t>(scan_rows(K)) * (segs * 12 + 12) + sizeof(SeqState);
+}
+
+struct ScanLds {
+    double *z;      // [rows * segs]
+    double *Z;      // [rows]
+    float *m;       // [rows * segs]
+    float *M;       // [rows]
+    SeqState *seq;
+
+    __device__ ScanLds(char *base, int K, int segs)
+    {
+        const int rows = scan_rows(K);
+        z = reinterpret_cast<double *>(base);
+        Z = z + static_cast<size_t>(rows) * segs;
+        seq = reinterpret_cast<SeqState *>(Z + rows);
+        m = reinterpret_cast<float *>(seq + 1);
+        M = m + static_cast<size_t>(rows) * segs;
+    }
+};
+
+template <typename E>
+__device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool publish, const ScanLds &S,
+                                           int &len_out)
+{
     const int t = threadIdx.x;
     const int lane = t & 63;
     const bool lead = t < 64;                 // wave 0 runs the per-position test
     const int K = p.K;
     const int segs = p.segs;
+    const int D0 = K + 1 < 64 ? K + 1 : 64;
     const int64_t row0 = static_cast<int64_t>(b) * (2 * K + 1);
-    const int nparts = kScanRows * segs;
     int n = -1;                               // known to wave 0
     bool oor = false;
     unsigned fl = 0;
     int len = K;
     for (int base = 0; base <= K; base += 64) {
+        const int nt = min(64, K + 1 - base);            // target rows of this block
+        const int nd = max(0, min(64, K - base));        // draft rows of this block
+        const int cnt = (nt + nd) * segs;
         const int k = base + lane;
         const int kc = max(0, min(k, K - 1));
         // the draft token first, so its logits can follow it (every wave
         // loads them; wave 0 uses them)
         const int x = p.draft[static_cast<int64_t>(b) * K + kc];
-        // every thread: its partials of target rows base.. and draft rows base..
+        // every thread: its partials of the block's rows
         SoftPartial q[kScanPer];
 #pragma unroll
         for (int j = 0; j < kScanPer; ++j) {
-            const int idx = min(t + j * kThreads, nparts - 1);
-            const int rr = idx / segs;
-            const int s = idx - rr * segs;
-            const int kk = base + (rr & 63);
-            const int ri = rr < 64 ? min(kk, K) : K + 1 + min(kk, K - 1);   // a row of this sequence
+            const int ci = min(t + j * kThreads, cnt - 1);
+            const int rc = ci / segs;
+            const int s = ci - rc * segs;
+            const int ri = rc < nt ? base + rc : K + 1 + base + (rc - nt);   // row within the sequence
             q[j] = p.partial[(row0 + ri) * segs + s];
         }
         const bool valid = K > 0 && x >= 0 && x < p.V;
@@ -243,41 +273,50 @@ __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
         len = p.has_len ? clamp_len(len_raw, K, fl) : K;
 #pragma unroll
         for (int j = 0; j < kScanPer; ++j) {
-            const int idx = t + j * kThreads;
-            if (idx < nparts) {
-                const int rr = idx / segs;
-                const int kk = base + (rr & 63);
-                const bool use = rr < 64 ? kk <= len : kk < len;
-                s_m[idx] = use ? q[j].m : -__builtin_inff();
-                s_z[idx] = use ? q[j].z : 0.0;
+            const int ci = t + j * kThreads;
+            if (ci < cnt) {
+                const int rc = ci / segs;
+                const int s = ci - rc * segs;
+                const bool tgt = rc < nt;
+                const int kk = base + (tgt ? rc : rc - nt);
+                const bool use = tgt ? kk <= len : kk < len;
+                const int slot = (tgt ? rc : D0 + rc - nt) * segs + s;
+                S.m[slot] = use ? q[j].m : -__builtin_inff();
+                S.z[slot] = use ? q[j].z : 0.0;
             }
         }
         __syncthreads();
-        if (t < kScanRows) {
+        const int srow = t < nt ? t : (t >= D0 && t < D0 + nd ? t : -1);   // an LDS row slot, or none
+        if (srow >= 0) {
             float M = -__builtin_inff();
             for (int s = 0; s < segs; ++s)
-                M = fmaxf(M, s_m[t * segs + s]);
-            s_M[t] = M;
+                M = fmaxf(M, S.m[srow * segs + s]);
+            S.M[srow] = M;
         }
         __syncthreads();
-        for (int idx = t; idx < nparts; idx += kThreads) {
-            const float m = s_m[idx];
-            const float M = s_M[idx / segs];
+        for (int ci = t; ci < cnt; ci += kThreads) {
+            const int rc = ci / segs;
+            const int s = ci - rc * segs;
+            const int slot_row = rc < nt ? rc : D0 + rc - nt;
+            const int slot = slot_row * segs + s;
+            const float m = S.m[slot];
+            const float M = S.M[slot_row];
             if (m != M)
-                s_z[idx] = rescale(s_z[idx], m, M, p.inv_t_d);
+                S.z[slot] = rescale(S.z[slot], m, M, p.inv_t_d);
         }
         __syncthreads();
-        if (t < kScanRows) {
+        if (srow >= 0) {
             double Z = 0.0;
             for (int s = 0; s < segs; ++s)
-                Z += s_z[t * segs + s];
-            s_Z[t] = Z;
+                Z += S.z[srow * segs + s];
+            S.Z[srow] = Z;
         }
         __syncthreads();
         if (lead) {
             oor |= k < len && !valid;
-            const double zt = s_Z[lane], zd = s_Z[64 + lane];
-            const float mt = s_M[lane], md = s_M[64 + lane];
+            const bool has_t = lane < nt, has_d = lane < nd;
+            const double zt = has_t ? S.Z[lane] : 0.0, zd = has_d ? S.Z[D0 + lane] : 0.0;
+            const float mt = has_t ? S.M[lane] : 0.0f, md = has_d ? S.M[D0 + lane] : 0.0f;
             double pk = 0.0, qk = 0.0;
             bool rejected = false;
             if (k < len) {
@@ -289,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
                 }
                 rejected = !(static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]) < ratio);
             }
-            if (k < K) {
+            if (publish && k < K) {
                 if (p.p_draft)
                     p.p_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(pk);
                 if (p.q_draft)
@@ -312,30 +351,44 @@ __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
                     sq.zd = zd;
                     sq.md = md;
                 }
-                p.seq[b] = sq;
+                *S.seq = sq;
+                if (publish)
+                    p.seq[b] = sq;
             }
             if (n < 0)
                 n = here;
         }
         __syncthreads();                      // LDS is restaged by the next block
     }
-    if (!lead)
-        return;
-    if (__ballot(oor))
-        fl |= SV_FLAG_DRAFT_OOR;
-    if (lane == 0) {
-        p.accepted[b] = n;
-        if (p.flags)
-            p.flags[b] = fl;
-        if (p.stats) {
-            stats_add(p.stats + 0, n);
-            stats_add(p.stats + 1, len);
-            stats_add(p.stats + 2, n + 1);
+    if (publish && lead) {
+        if (__ballot(oor))
+            fl |= SV_FLAG_DRAFT_OOR;
+        if (lane == 0) {
+            p.accepted[b] = n;
+            if (p.flags)
+                p.flags[b] = fl;
+            if (p.stats) {
+                stats_add(p.stats + 0, n);
+                stats_add(p.stats + 1, len);
+                stats_add(p.stats + 2, n + 1);
+            }
         }
+        if (p.stats)
+            for (int k = lane; k < n; k += 64)
+                stats_add(p.stats + 3 + k, 1);
     }
-    if (p.stats)
-        for (int k = lane; k < n; k += 64)
-            stats_add(p.stats + 3 + k, 1);
+    len_out = len;
+    return *S.seq;                            // written before the last barrier
+}
+
+// Kernel 2: one workgroup per sequence.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
+{
+    extern __shared__ __align__(16) char s_dyn[];
+    const ScanLds S(s_dyn, p.K, p.segs);
+    int len;
+    decide<E>(p, blockIdx.x, true, S, len);
 }
 
 // kN consecutive elements [v0, v0 + kN) of a row, loaded before use.  kVec:
@@ -445,17 +498,11 @@ struct SampleRows {
     }
 };
 
-// Kernel 3: one workgroup per (sequence, chunk); two memory rounds (the
-// sequence state, then both rows' slices).
+// The final-sample masses of one chunk of row pair n (step a5): p and
+// r = max(0, p - q) per element, one mass pair per 1024-element sub-chunk.
 template <typename E, bool kVec>
-__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
+__device__ __forceinline__ void chunk_masses(const RejectParams &p, int b, int c, int len, const SeqState &st)
 {
-    const int b = blockIdx.x / p.nchunks;
-    const int c = blockIdx.x - b * p.nchunks;
-    const int len_raw = p.draft_len[b];
-    const SeqState st = p.seq[b];
-    unsigned unused = 0;
-    const int len = p.has_len ? clamp_len(len_raw, p.K, unused) : p.K;
     const SampleRows<E> sr(p, b, len, st);
     const int v0 = c * kRejChunk + threadIdx.x * kChunkPerThread;
     const int cnt = max(0, min(kChunkPerThread, p.V - v0));
@@ -469,6 +516,20 @@ __global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
     if ((threadIdx.x & 63) == 0)
         p.cmass[(static_cast<int64_t>(b) * p.nchunks + c) * kSubPerChunk + (threadIdx.x >> 6)] =
             ChunkMass{rs, ps};
+}
+
+// Kernel 3: one workgroup per (sequence, chunk); two memory rounds (the
+// sequence state, then both rows' slices).
+template <typename E, bool kVec>
+__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
+{
+    const int b = blockIdx.x / p.nchunks;
+    const int c = blockIdx.x - b * p.nchunks;
+    const int len_raw = p.draft_len[b];
+    const SeqState st = p.seq[b];
+    unsigned unused = 0;
+    const int len = p.has_len ? clamp_len(len_raw, p.K, unused) : p.K;
+    chunk_masses<E, kVec>(p, b, c, len, st);
 }
 
 // Kernel 4: one workgroup per sequence, two memory rounds.  Round 1 loads
@@ -605,7 +666,8 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_rej_scan<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    const size_t lds = scan_lds_bytes(p.K, p.segs);
+    hipLaunchKernelGGL(k_rej_scan<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));

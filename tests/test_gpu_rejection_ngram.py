@@ -99,6 +99,17 @@ def test_rejection_extreme_logits(orc, case, dtype):
     _rej_case(orc, wl, label="extreme %s %s" % (case, dtype))
 
 
+@pytest.mark.parametrize("K", [63, 64, 130])
+def test_rejection_long_drafts(orc, K):
+    """Draft lengths at and past one 64-position block of the accept scan
+    (which works in blocks of 64 positions), with and without per-sequence
+    lengths."""
+    wl = W.rejection_workload(4, K, 3000, 2.0, 0.15, 1.0, seed=700 + K, dtype="bf16")
+    _rej_case(orc, wl, label="K%d" % K)
+    dl = np.array([K, 0, K // 2, 65], np.int32)
+    _rej_case(orc, wl, draft_len=dl, label="K%d ragged" % K)
+
+
 def test_rejection_split_rows_and_repeat(orc):
     sv.set_tuning(sv.TUNE_MIN_SEGMENT_BYTES, 2048)
     try:
