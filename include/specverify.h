@@ -206,6 +206,58 @@ int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Vocabulary-sharded verification (logits split by vocabulary range, as a
+ * tensor-parallel output layer leaves them).  Greedy and tree verification
+ * need only each row's maximum and its lowest id, and those merge across
+ * shards in the same total order (larger value, then lower id), so each
+ * shard reduces its columns to one partial per row and the verification
+ * runs on the partials.  On one device this is a split of the streaming
+ * pass; across devices the partials (8 bytes per row and shard) are what an
+ * all-gather would exchange.
+ *
+ * sv_argmax_shard -- per-row partial of one shard:
+ *   out[r].value = max_v logits[r][v], out[r].index = v_offset + the lowest
+ *   v holding it, over v in [0, V) of the shard; a row with no value above
+ *   -inf gives {-inf, SV_NO_INDEX}.
+ *   logits [rows][row_stride] (the shard's columns; row_stride >= V)
+ *   v_offset  the shard's first global token id (0 <= v_offset,
+ *             v_offset + V <= SV_MAX_V)
+ *   out [rows] sv_argmax_partial (out; 8-byte aligned)
+ *   workspace as sized by sv_argmax_shard_workspace_bytes.
+ *
+ * sv_verify_greedy_partials / sv_verify_tree_partials -- sv_verify_greedy /
+ * sv_verify_tree on shard partials: partials [P][rows] with rows = B*(K+1)
+ * (greedy) or B*N (tree), shard p's row r at partials[p * rows + r]; V is
+ * the full vocabulary (draft ids outside [0, V) never match).  The results
+ * equal those of the unsharded call on the concatenated logits.  No
+ * workspace.  Limits: 1 <= P <= SV_MAX_SHARDS, and those of the unsharded
+ * calls.
+ */
+typedef struct {
+    float value;
+    int32_t index;
+} sv_argmax_partial;
+
+#define SV_NO_INDEX 0x7fffffff      /* index of a partial whose row is all -inf */
+#define SV_MAX_SHARDS 4096          /* P of the *_partials calls */
+
+size_t sv_argmax_shard_workspace_bytes(int32_t rows, int32_t V);
+int sv_argmax_shard(const void *logits, int32_t dtype, int64_t row_stride,
+                    int32_t rows, int32_t V, int32_t v_offset,
+                    sv_argmax_partial *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int sv_verify_greedy_partials(const sv_argmax_partial *partials, int32_t P,
+                              const int32_t *draft, const int32_t *draft_len,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t *accepted, int32_t *emitted, int32_t *argmax_out,
+                              uint32_t *flags, int64_t *stats, void *stream);
+int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
+                            const int32_t *parent, const int32_t *token,
+                            int32_t B, int32_t N, int32_t V,
+                            int32_t *accepted, int32_t *path, int32_t *emitted,
+                            int32_t *argmax_out, uint32_t *flags, void *stream);
+
+/*
  * sv_ngram_propose -- [Handbook] "N-gram" (take a suffix, find an earlier
  * occurrence, copy what followed), [vLLM-03] "2. draft methods"
  * (prompt_lookup_max down to prompt_lookup_min) and "3-1" (no match, no

@@ -19,6 +19,8 @@ import ctypes
 import os
 import threading
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
@@ -31,7 +33,15 @@ TUNE_TARGET_WORKGROUPS, TUNE_MIN_SEGMENT_BYTES = 1, 2
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_set_tuning",
            "sv_greedy_workspace_bytes", "sv_verify_greedy",
            "sv_rejection_workspace_bytes", "sv_verify_rejection",
-           "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose")
+           "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose",
+           "sv_argmax_shard_workspace_bytes", "sv_argmax_shard",
+           "sv_verify_greedy_partials", "sv_verify_tree_partials")
+
+# One sv_argmax_partial: the row's largest value and the lowest global token
+# id holding it (NO_INDEX when the shard's row is all -inf).  The binding
+# keeps partials in int64 tensors, one element per partial.
+PARTIAL_DTYPE = np.dtype([("value", "<f4"), ("index", "<i4")])
+NO_INDEX = 0x7FFFFFFF
 
 
 class SpecVerifyError(RuntimeError):
@@ -79,6 +89,14 @@ def load(path: str = LIB_PATH):
         L.sv_verify_tree.argtypes = [P, i32, i64, P, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
         L.sv_ngram_propose.restype = ctypes.c_int
         L.sv_ngram_propose.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P, P, P]
+        L.sv_argmax_shard_workspace_bytes.restype = sz
+        L.sv_argmax_shard_workspace_bytes.argtypes = [i32, i32]
+        L.sv_argmax_shard.restype = ctypes.c_int
+        L.sv_argmax_shard.argtypes = [P, i32, i64, i32, i32, i32, P, P, sz, P]
+        L.sv_verify_greedy_partials.restype = ctypes.c_int
+        L.sv_verify_greedy_partials.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P, P, P]
+        L.sv_verify_tree_partials.restype = ctypes.c_int
+        L.sv_verify_tree_partials.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         _lib = L
         return L
 
@@ -306,3 +324,98 @@ def prepare_ngram(tokens, lengths, n_min, n_max, K):
 
 def ngram_propose(*a, **k):
     return prepare_ngram(*a, **k)()
+
+
+# ---------------------------------------------------------------- vocabulary shards
+
+def prepare_argmax_shard(logits, v_offset, out=None):
+    """Per-row partial of one vocabulary shard: logits [..., Vs] (evenly
+    spaced rows, unit stride along the shard's columns, e.g. a column slice
+    of the full logits), v_offset = the shard's first global token id.
+    Output: partial, an int64 tensor [rows] of sv_argmax_partial (decode
+    with PARTIAL_DTYPE); pass `out` (a contiguous int64 [rows] tensor, e.g.
+    one row of a [P, rows] tensor) to write in place."""
+    torch = _torch()
+    L = load()
+    code, rs = _logits_args(logits, "logits", logits.dim() - 1)
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    dev = logits.device
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int64, device=dev)
+    elif out.dtype != torch.int64 or not out.is_contiguous() or out.numel() != rows:
+        raise ValueError("out must be a contiguous int64 tensor of %d elements" % rows)
+    s = _stream(dev)
+    ws = workspace(L.sv_argmax_shard_workspace_bytes(rows, V), dev, s)
+    args = (logits.data_ptr(), code, rs, rows, V, int(v_offset), out.data_ptr(), ws.data_ptr(),
+            ws.numel(), s)
+    return Prepared(L.sv_argmax_shard, args, dict(partial=out), (logits, out, ws))
+
+
+def argmax_shard(*a, **k):
+    return prepare_argmax_shard(*a, **k)()
+
+
+def _partials(partials, rows):
+    torch = _torch()
+    if partials.dtype != torch.int64 or partials.dim() != 2 or not partials.is_contiguous() \
+            or partials.shape[1] != rows:
+        raise ValueError("partials must be a contiguous int64 [P, %d] tensor" % rows)
+    return partials.shape[0]
+
+
+def prepare_greedy_partials(partials, draft, V, draft_len=None, *, want_argmax=True, stats=None):
+    """Greedy verification from vocabulary-shard partials [P, B*(K+1)]
+    (shard p's partials in row p), draft [B, K] int32, V = the full
+    vocabulary.  Outputs as prepare_greedy."""
+    torch = _torch()
+    L = load()
+    B, K = draft.shape
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    Pn = _partials(partials, B * (K + 1))
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 3 + K):
+        raise ValueError("stats must be an int64 tensor of at least 3+K entries")
+    dev = partials.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    amx = torch.empty(B, K + 1, dtype=torch.int32, device=dev) if want_argmax else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    args = (partials.data_ptr(), Pn, _ptr(draft), _ptr(draft_len), B, K, int(V), acc.data_ptr(),
+            emi.data_ptr(), _ptr(amx), flg.data_ptr(), _ptr(stats), _stream(dev))
+    out = dict(accepted=acc, emitted=emi, flags=flg)
+    if want_argmax:
+        out["argmax"] = amx
+    return Prepared(L.sv_verify_greedy_partials, args, out, (partials, draft, draft_len, stats))
+
+
+def verify_greedy_partials(*a, **k):
+    return prepare_greedy_partials(*a, **k)()
+
+
+def prepare_tree_partials(partials, parent, token, V, *, want_argmax=True):
+    """Tree verification from vocabulary-shard partials [P, B*N], parent
+    and token [B, N] int32, V = the full vocabulary.  Outputs as
+    prepare_tree."""
+    torch = _torch()
+    L = load()
+    B, N = parent.shape
+    _i32(parent, (B, N), "parent")
+    _i32(token, (B, N), "token")
+    Pn = _partials(partials, B * N)
+    dev = partials.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty(B, N, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, N, dtype=torch.int32, device=dev)
+    amx = torch.empty(B, N, dtype=torch.int32, device=dev) if want_argmax else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    args = (partials.data_ptr(), Pn, parent.data_ptr(), token.data_ptr(), B, N, int(V),
+            acc.data_ptr(), path.data_ptr(), emi.data_ptr(), _ptr(amx), flg.data_ptr(), _stream(dev))
+    out = dict(accepted=acc, path=path, emitted=emi, flags=flg)
+    if want_argmax:
+        out["argmax"] = amx
+    return Prepared(L.sv_verify_tree_partials, args, out, (partials, parent, token))
+
+
+def verify_tree_partials(*a, **k):
+    return prepare_tree_partials(*a, **k)()

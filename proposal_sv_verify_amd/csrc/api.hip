@@ -13,6 +13,8 @@
 #include <string>
 
 #include "specverify.h"
+
+#include <cstddef>
 #include "sv_kernels.hpp"
 
 namespace {
@@ -369,6 +371,171 @@ int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
     hipError_t e = sv::launch_tree(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "tree launch");
+    return SV_OK;
+}
+
+// ------------------------------------------------------------------ vocabulary shards
+
+static_assert(sizeof(sv_argmax_partial) == sizeof(sv::ArgPartial) &&
+                  offsetof(sv_argmax_partial, value) == offsetof(sv::ArgPartial, v) &&
+                  offsetof(sv_argmax_partial, index) == offsetof(sv::ArgPartial, i),
+              "the public shard partial is the kernels' partial");
+static_assert(SV_NO_INDEX == 0x7fffffff, "the kernels' 'no index' value");
+
+size_t sv_argmax_shard_workspace_bytes(int32_t rows, int32_t V)
+{
+    if (rows < 1 || V < 1)
+        return 0;
+    const RowPlan a = plan_rows(rows, V, 2);
+    const RowPlan b = plan_rows(rows, V, 4);
+    const size_t x = arg_layout(1, rows, a).total, y = arg_layout(1, rows, b).total;
+    return x > y ? x : y;
+}
+
+int sv_argmax_shard(const void *logits, int32_t dtype, int64_t row_stride,
+                    int32_t rows, int32_t V, int32_t v_offset,
+                    sv_argmax_partial *out,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if (rows < 1)
+        return fail(SV_ERR_INVALID_ARG, "rows = %d < 1", rows);
+    if (V < 1)
+        return fail(SV_ERR_INVALID_ARG, "V = %d < 1", V);
+    if (v_offset < 0)
+        return fail(SV_ERR_INVALID_ARG, "v_offset = %d < 0", v_offset);
+    if (static_cast<int64_t>(v_offset) + V > SV_MAX_V)
+        return fail(SV_ERR_UNSUPPORTED, "v_offset + V = %lld above %d",
+                    static_cast<long long>(v_offset) + V, SV_MAX_V);
+    if ((st = check_logits(logits, dtype, row_stride, V, "logits")) != SV_OK)
+        return st;
+    if (!out || misaligned(out, 8))
+        return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const ArgLayout L = arg_layout(1, rows, pl);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    if ((st = check_grid(static_cast<int64_t>(rows) * pl.segs)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::ArgVerifyParams p{};
+    p.logits = logits;
+    p.row_stride = row_stride;
+    p.B = 1;
+    p.V = V;
+    p.rows_per_seq = rows;
+    p.segs = pl.segs;
+    p.seg_len = pl.seg_len;
+    p.partial = at<sv::ArgPartial>(workspace, L.partial);
+    p.v_offset = v_offset;
+    p.shard_out = reinterpret_cast<sv::ArgPartial *>(out);
+    hipError_t e = sv::launch_argmax_shard(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "shard argmax launch");
+    return SV_OK;
+}
+
+namespace {
+
+int check_partials(const sv_argmax_partial *partials, int32_t P)
+{
+    if (P < 1)
+        return fail(SV_ERR_INVALID_ARG, "P = %d < 1", P);
+    if (P > SV_MAX_SHARDS)
+        return fail(SV_ERR_UNSUPPORTED, "P = %d above %d", P, SV_MAX_SHARDS);
+    if (!partials || misaligned(partials, 8))
+        return fail(SV_ERR_INVALID_ARG, "partials must be non-NULL and 8-byte aligned");
+    return SV_OK;
+}
+
+} // namespace
+
+int sv_verify_greedy_partials(const sv_argmax_partial *partials, int32_t P,
+                              const int32_t *draft, const int32_t *draft_len,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t *accepted, int32_t *emitted, int32_t *argmax_out,
+                              uint32_t *flags, int64_t *stats, void *stream)
+{
+    int st;
+    if ((st = check_sizes(B, K, V)) != SV_OK)
+        return st;
+    if ((st = check_partials(partials, P)) != SV_OK)
+        return st;
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if (!accepted || !emitted)
+        return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::ArgVerifyParams p{};
+    p.B = B;
+    p.V = V;
+    p.rows_per_seq = K + 1;
+    p.segs = P;
+    p.partial_in = reinterpret_cast<const sv::ArgPartial *>(partials);
+    p.part_row_step = 1;
+    p.part_seg_step = static_cast<int64_t>(B) * (K + 1);
+    p.draft = draft;
+    p.draft_len = draft_len;
+    p.K = K;
+    p.stats = stats;
+    p.accepted = accepted;
+    p.emitted = emitted;
+    p.argmax_out = argmax_out;
+    p.flags = flags;
+    hipError_t e = sv::launch_greedy_scan(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "greedy scan launch");
+    return SV_OK;
+}
+
+int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
+                            const int32_t *parent, const int32_t *token,
+                            int32_t B, int32_t N, int32_t V,
+                            int32_t *accepted, int32_t *path, int32_t *emitted,
+                            int32_t *argmax_out, uint32_t *flags, void *stream)
+{
+    int st;
+    if (B < 1)
+        return fail(SV_ERR_INVALID_ARG, "B = %d < 1", B);
+    if (N < 1)
+        return fail(SV_ERR_INVALID_ARG, "N = %d < 1", N);
+    if (V < 1)
+        return fail(SV_ERR_INVALID_ARG, "V = %d < 1", V);
+    if (N > SV_MAX_TREE_NODES)
+        return fail(SV_ERR_UNSUPPORTED, "N = %d above %d", N, SV_MAX_TREE_NODES);
+    if (V > SV_MAX_V)
+        return fail(SV_ERR_UNSUPPORTED, "V = %d above %d", V, SV_MAX_V);
+    if ((st = check_partials(partials, P)) != SV_OK)
+        return st;
+    if (!parent || !token)
+        return fail(SV_ERR_INVALID_ARG, "parent and token are required");
+    if (!accepted || !path || !emitted)
+        return fail(SV_ERR_INVALID_ARG, "accepted, path and emitted are required");
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::ArgVerifyParams p{};
+    p.B = B;
+    p.V = V;
+    p.rows_per_seq = N;
+    p.segs = P;
+    p.partial_in = reinterpret_cast<const sv::ArgPartial *>(partials);
+    p.part_row_step = 1;
+    p.part_seg_step = static_cast<int64_t>(B) * N;
+    p.parent = parent;
+    p.token = token;
+    p.path = path;
+    p.accepted = accepted;
+    p.emitted = emitted;
+    p.argmax_out = argmax_out;
+    p.flags = flags;
+    hipError_t e = sv::launch_tree_scan(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "tree scan launch");
     return SV_OK;
 }
 

@@ -65,14 +65,29 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(const ArgVerifyParams p
 // the maximum.
 __device__ __forceinline__ int merged_argmax(const ArgVerifyParams &p, int64_t row)
 {
-    const ArgPartial *pp = p.partial + row * p.segs;
+    const ArgPartial *pp = p.partial_in + row * p.part_row_step;
     float bv = -__builtin_inff();
     int bi = kIdxNone;
     for (int s = 0; s < p.segs; ++s) {
-        const ArgPartial q = pp[s];
+        const ArgPartial q = pp[s * p.part_seg_step];
         arg_combine(bv, bi, q.v, q.i);
     }
     return bi == kIdxNone ? 0 : bi;
+}
+
+// A shard's per-row partial: its segments merged, the index moved to the
+// global vocabulary (a row with nothing above -inf keeps "none").
+__global__ __launch_bounds__(kThreads) void k_shard_rows(const ArgVerifyParams p)
+{
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (row >= static_cast<int64_t>(p.B) * p.rows_per_seq)
+        return;
+    const ArgPartial *pp = p.partial + row * p.segs;
+    float bv = -__builtin_inff();
+    int bi = kIdxNone;
+    for (int s = 0; s < p.segs; ++s)
+        arg_combine(bv, bi, pp[s].v, pp[s].i);
+    p.shard_out[row] = ArgPartial{bv, bi == kIdxNone ? kIdxNone : bi + p.v_offset};
 }
 
 // One wave per sequence, one lane per position (in blocks of 64 positions).
@@ -262,14 +277,29 @@ hipError_t launch_rows(const ArgVerifyParams &p, int dtype, hipStream_t s)
 
 } // namespace
 
+hipError_t launch_greedy_scan(const ArgVerifyParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_greedy_scan, dim3(static_cast<unsigned>((p.B + kWaves - 1) / kWaves)),
+                       dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_scan(const ArgVerifyParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tree_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_greedy(const ArgVerifyParams &p, int dtype, hipStream_t s)
 {
     hipError_t e = launch_rows(p, dtype, s);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_greedy_scan, dim3(static_cast<unsigned>((p.B + kWaves - 1) / kWaves)),
-                       dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+    ArgVerifyParams q = p;
+    q.partial_in = p.partial;
+    q.part_row_step = p.segs;
+    q.part_seg_step = 1;
+    return launch_greedy_scan(q, s);
 }
 
 hipError_t launch_tree(const ArgVerifyParams &p, int dtype, hipStream_t s)
@@ -279,7 +309,22 @@ hipError_t launch_tree(const ArgVerifyParams &p, int dtype, hipStream_t s)
     hipError_t e = launch_rows(q, dtype, s);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_tree_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, q);
+    q.partial_in = p.partial;
+    q.part_row_step = p.segs;
+    q.part_seg_step = 1;
+    return launch_tree_scan(q, s);
+}
+
+hipError_t launch_argmax_shard(const ArgVerifyParams &p, int dtype, hipStream_t s)
+{
+    ArgVerifyParams q = p;
+    q.draft_len = nullptr;          // every row is needed
+    hipError_t e = launch_rows(q, dtype, s);
+    if (e != hipSuccess)
+        return e;
+    const int64_t rows = static_cast<int64_t>(p.B) * p.rows_per_seq;
+    hipLaunchKernelGGL(k_shard_rows, dim3(static_cast<unsigned>((rows + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, q);
     return hipGetLastError();
 }
 

@@ -68,12 +68,23 @@ struct ArgVerifyParams {
     int32_t *emitted;
     int32_t *argmax_out;    // [B * rows_per_seq] or null
     uint32_t *flags;
-    // workspace
-    ArgPartial *partial;    // [rows * segs]
+    // workspace: the partial of (row, segment s) is partial[row * part_row_step
+    // + s * part_seg_step]; segments of one row are merged in the total order
+    const ArgPartial *partial_in;
+    ArgPartial *partial;    // written by the row kernel: [rows * segs]
+    int64_t part_row_step, part_seg_step;
+    // per-row partials of a vocabulary shard
+    int32_t v_offset;
+    ArgPartial *shard_out;  // [rows]
 };
 
 hipError_t launch_greedy(const ArgVerifyParams &p, int dtype, hipStream_t s);
 hipError_t launch_tree(const ArgVerifyParams &p, int dtype, hipStream_t s);
+// the per-sequence kernels alone, on partials the caller supplies
+hipError_t launch_greedy_scan(const ArgVerifyParams &p, hipStream_t s);
+hipError_t launch_tree_scan(const ArgVerifyParams &p, hipStream_t s);
+// per-row (max, argmax + v_offset) of a vocabulary shard into shard_out
+hipError_t launch_argmax_shard(const ArgVerifyParams &p, int dtype, hipStream_t s);
 
 // Rejection sampling.  Rows per sequence: K+1 target rows then K draft rows.
 struct RejectParams {

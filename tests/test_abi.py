@@ -152,3 +152,49 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(sv, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         sv.load(str(tmp_path / "nope.so"))
+
+
+def test_shard_calls_reject_bad_arguments(lib):
+    def shard(**kw):
+        a = dict(l=FAKE, dtype=1, rs=100, rows=8, V=100, off=0, out=FAKE, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_argmax_shard(a["l"], a["dtype"], a["rs"], a["rows"], a["V"], a["off"],
+                                   a["out"], a["ws"], a["wsb"], None)
+    assert shard(rows=0) == sv.SV_ERR_INVALID_ARG
+    assert shard(V=0) == sv.SV_ERR_INVALID_ARG
+    assert shard(off=-1) == sv.SV_ERR_INVALID_ARG
+    assert shard(off=(1 << 30) - 50) == sv.SV_ERR_UNSUPPORTED     # shard past SV_MAX_V
+    assert shard(rs=99) == sv.SV_ERR_INVALID_ARG
+    assert shard(out=None) == sv.SV_ERR_INVALID_ARG
+    assert shard(out=FAKE + 4) == sv.SV_ERR_INVALID_ARG            # partials are 8-byte aligned
+    assert shard(wsb=8) == sv.SV_ERR_WORKSPACE
+    assert lib.sv_argmax_shard_workspace_bytes(0, 100) == 0
+    assert lib.sv_argmax_shard_workspace_bytes(64, 32000) > 0
+
+    def greedy(**kw):
+        a = dict(parts=FAKE, P=4, draft=FAKE, dl=None, B=2, K=3, V=100, acc=FAKE, emi=FAKE)
+        a.update(kw)
+        return lib.sv_verify_greedy_partials(a["parts"], a["P"], a["draft"], a["dl"], a["B"],
+                                             a["K"], a["V"], a["acc"], a["emi"], None, None,
+                                             None, None)
+    assert greedy(P=0) == sv.SV_ERR_INVALID_ARG
+    assert greedy(P=5000) == sv.SV_ERR_UNSUPPORTED
+    assert greedy(parts=None) == sv.SV_ERR_INVALID_ARG
+    assert greedy(parts=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert greedy(B=0) == sv.SV_ERR_INVALID_ARG
+    assert greedy(draft=None) == sv.SV_ERR_INVALID_ARG
+    assert greedy(emi=None) == sv.SV_ERR_INVALID_ARG
+
+    def tree(**kw):
+        a = dict(parts=FAKE, P=2, par=FAKE, tok=FAKE, B=2, N=8, V=100, acc=FAKE, path=FAKE,
+                 emi=FAKE)
+        a.update(kw)
+        return lib.sv_verify_tree_partials(a["parts"], a["P"], a["par"], a["tok"], a["B"],
+                                           a["N"], a["V"], a["acc"], a["path"], a["emi"], None,
+                                           None, None)
+    assert tree(P=0) == sv.SV_ERR_INVALID_ARG
+    assert tree(N=2000) == sv.SV_ERR_UNSUPPORTED
+    assert tree(tok=None) == sv.SV_ERR_INVALID_ARG
+    assert tree(path=None) == sv.SV_ERR_INVALID_ARG
+    for f in (shard, greedy, tree):
+        assert lib.sv_last_error_message()
