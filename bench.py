@@ -156,6 +156,49 @@ def ngram_bandwidth_mode(args):
                 gb_per_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
 
 
+def greedy_shards(gr, shards=8, reps=30):
+    """The large greedy workload as an 8-way vocabulary-sharded output layer
+    would hold it: sv_argmax_shard on each 18992-column slice, then
+    sv_verify_greedy_partials, beside the unsharded call on the same
+    logits.  Times are HIP-event means over `reps` repetitions."""
+    import torch
+    import proposal_sv_verify_amd as sv
+
+    dev = torch.device("cuda:0")
+    lg = torch.from_numpy(gr["logits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    dr = torch.from_numpy(gr["drafts"][0.6]).to(dev)
+    V = lg.shape[-1]
+    rows = lg.shape[0] * lg.shape[1]
+    cuts = [(i * V // shards, (i + 1) * V // shards) for i in range(shards)]
+    parts = torch.empty(shards, rows, dtype=torch.int64, device=dev)
+    shard_calls = [sv.prepare_argmax_shard(lg[..., a:b], a, out=parts[p]) for p, (a, b) in enumerate(cuts)]
+    combine = sv.prepare_greedy_partials(parts, dr, V)
+    whole = sv.prepare_greedy(lg, dr)
+
+    def timed(fns):
+        for _ in range(3):
+            for f in fns:
+                f()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            for f in fns:
+                f()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    t_shards = timed(shard_calls)
+    t_combine = timed([combine])
+    t_whole = timed([whole])
+    same = all(torch.equal(combine()[k], whole()[k]) for k in ("accepted", "emitted", "argmax"))
+    nbytes = rows * V * 2
+    return dict(shards=shards, us_shard_calls=round(t_shards, 2), us_combine=round(t_combine, 2),
+                us_unsharded=round(t_whole, 2),
+                gb_per_s_shard_calls=round(nbytes / t_shards / 1e3, 1), same_result=bool(same))
+
+
 def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
     """The oracle, as it stands, on the host cores: whole steps (all four
     calls, every sequence), sequences spread over a thread pool, for at
@@ -254,6 +297,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-bandwidth-mode", action="store_true",
                     help="skip the 16384-context n-gram measurement")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip the vocabulary-sharded greedy measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy a 256 MiB device buffer three times (a "
                          "kernel of known traffic for scaling the rocprofv3 byte counters)")
@@ -309,6 +354,8 @@ def main():
                   roofline=roofline, kernels=kernels)
     if not args.no_bandwidth_mode:
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
+    if not args.no_shards:
+        result["greedy_vocab_shards"] = greedy_shards(gr)
     if not args.no_cpu:
         cb, parity = cpu_baseline(ng, rj, gr, tr, args.cpu_seconds, outs)
         result["cpu_baseline"] = cb

@@ -56,8 +56,12 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(const ArgVerifyParams p
             });
     }
     block_argmax(bv, bi);
-    if (threadIdx.x == 0)
-        p.partial[static_cast<int64_t>(row) * p.segs + seg] = ArgPartial{bv, bi};
+    if (threadIdx.x == 0) {
+        if (p.shard_out != nullptr && p.segs == 1)   // a shard's row in one segment: final already
+            p.shard_out[row] = ArgPartial{bv, bi == kIdxNone ? kIdxNone : bi + p.v_offset};
+        else
+            p.partial[static_cast<int64_t>(row) * p.segs + seg] = ArgPartial{bv, bi};
+    }
 }
 
 // Row argmax from its segment partials.  A row whose elements all compare
@@ -320,8 +324,8 @@ hipError_t launch_argmax_shard(const ArgVerifyParams &p, int dtype, hipStream_t 
     ArgVerifyParams q = p;
     q.draft_len = nullptr;          // every row is needed
     hipError_t e = launch_rows(q, dtype, s);
-    if (e != hipSuccess)
-        return e;
+    if (e != hipSuccess || p.segs == 1)
+        return e;                   // one segment per row: the row kernel wrote shard_out
     const int64_t rows = static_cast<int64_t>(p.B) * p.rows_per_seq;
     hipLaunchKernelGGL(k_shard_rows, dim3(static_cast<unsigned>((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, s, q);
