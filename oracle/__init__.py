@@ -206,3 +206,31 @@ def verify_tree(*a, **k):
 
 def ngram_propose(*a, **k):
     return default().ngram_propose(*a, **k)
+
+
+# ---------------------------------------------------------------- adaptive length
+
+def adaptive_tier(ema, tiers):
+    """The speculation length for an acceptance-length average `ema`: the
+    smallest tier strictly above it (room for one more token than the usual
+    accepted run), else the largest tier."""
+    for t in tiers:
+        if t > ema:
+            return t
+    return tiers[-1]
+
+
+def adaptive_lengths(accepted_means, tiers=(1, 3, 7), beta=0.2, ema0=0.0):
+    """[Handbook] "adaptive" (SGLang's mechanism): after each verification
+    round, an exponential moving average of the number of accepted draft
+    tokens is updated, ema <- (1 - beta) * ema + beta * accepted, and the next
+    round's speculation length is chosen among fixed tiers from it.  Returns
+    the length used in each round (the first from ema0) and the averages
+    after each round."""
+    ema = float(ema0)
+    ks, emas = [], []
+    for a in accepted_means:
+        ks.append(adaptive_tier(ema, tiers))
+        ema = (1.0 - beta) * ema + beta * float(a)
+        emas.append(ema)
+    return ks, emas
