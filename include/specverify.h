@@ -258,6 +258,39 @@ int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
                             int32_t *argmax_out, uint32_t *flags, void *stream);
 
 /*
+ * Adaptive speculation length -- [Handbook] "adaptive" (the mechanism it
+ * describes for SGLang): after each verification round, the mean number of
+ * accepted draft tokens per sequence updates an exponential moving average,
+ * ema <- (1 - beta) * ema + beta * accepted_mean, and the next round's
+ * speculation length K is chosen from fixed tiers (the pages' default is
+ * 1, 3, 7): the smallest tier of at least 2 * ema, else the largest.  Only
+ * K changes, never the verification, so the output is unchanged.  Host code:
+ * the state is a caller-owned host struct; nothing touches the GPU.  The
+ * round's accepted_mean is, e.g., the growth of a verifier's stats[0]
+ * divided by the number of sequences.
+ *
+ * sv_adaptive_init: tiers strictly increasing in [1, SV_MAX_DRAFTS],
+ *   1 <= ntiers <= SV_MAX_TIERS, 0 < beta <= 1, ema0 finite and >= 0;
+ *   sets state->k to the first round's length.
+ * sv_adaptive_update: accepted_mean finite and >= 0; sets state->ema and
+ *   state->k (the next round's length).
+ * Both return SV_OK or SV_ERR_INVALID_ARG (state unchanged).
+ */
+#define SV_MAX_TIERS 16
+
+typedef struct {
+    double ema;                      /* moving average of accepted drafts per sequence */
+    double beta;                     /* smoothing factor */
+    int32_t ntiers;
+    int32_t tiers[SV_MAX_TIERS];
+    int32_t k;                       /* speculation length for the next round */
+} sv_adaptive;
+
+int sv_adaptive_init(sv_adaptive *state, const int32_t *tiers, int32_t ntiers, double beta,
+                     double ema0);
+int sv_adaptive_update(sv_adaptive *state, double accepted_mean);
+
+/*
  * sv_ngram_propose -- [Handbook] "N-gram" (take a suffix, find an earlier
  * occurrence, copy what followed), [vLLM-03] "2. draft methods"
  * (prompt_lookup_max down to prompt_lookup_min) and "3-1" (no match, no

@@ -212,10 +212,14 @@ def ngram_propose(*a, **k):
 
 def adaptive_tier(ema, tiers):
     """The speculation length for an acceptance-length average `ema`: the
-    smallest tier strictly above it (room for one more token than the usual
-    accepted run), else the largest tier."""
+    smallest tier of at least 2 * ema, else the largest tier -- as much room
+    above the usual accepted run as the run itself uses.  The average can
+    never exceed the length in use, so the rule must move up before the
+    average reaches the next tier (from length 1: once drafts are accepted
+    more often than not) and back down before it reaches 0 (to length 1:
+    once the average run is half a token)."""
     for t in tiers:
-        if t > ema:
+        if t >= 2.0 * ema:
             return t
     return tiers[-1]
 

@@ -35,7 +35,8 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_se
            "sv_rejection_workspace_bytes", "sv_verify_rejection",
            "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose",
            "sv_argmax_shard_workspace_bytes", "sv_argmax_shard",
-           "sv_verify_greedy_partials", "sv_verify_tree_partials")
+           "sv_verify_greedy_partials", "sv_verify_tree_partials",
+           "sv_adaptive_init", "sv_adaptive_update")
 
 # One sv_argmax_partial: the row's largest value and the lowest global token
 # id holding it (NO_INDEX when the shard's row is all -inf).  The binding
@@ -95,6 +96,10 @@ def load(path: str = LIB_PATH):
         L.sv_argmax_shard.argtypes = [P, i32, i64, i32, i32, i32, P, P, sz, P]
         L.sv_verify_greedy_partials.restype = ctypes.c_int
         L.sv_verify_greedy_partials.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P, P, P]
+        L.sv_adaptive_init.restype = ctypes.c_int
+        L.sv_adaptive_init.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
+        L.sv_adaptive_update.restype = ctypes.c_int
+        L.sv_adaptive_update.argtypes = [P, ctypes.c_double]
         L.sv_verify_tree_partials.restype = ctypes.c_int
         L.sv_verify_tree_partials.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         _lib = L
@@ -419,3 +424,33 @@ def prepare_tree_partials(partials, parent, token, V, *, want_argmax=True):
 
 def verify_tree_partials(*a, **k):
     return prepare_tree_partials(*a, **k)()
+
+
+# ---------------------------------------------------------------- adaptive length
+
+class _AdaptiveState(ctypes.Structure):
+    _fields_ = [("ema", ctypes.c_double), ("beta", ctypes.c_double), ("ntiers", ctypes.c_int32),
+                ("tiers", ctypes.c_int32 * 16), ("k", ctypes.c_int32)]
+
+
+class Adaptive:
+    """Adaptive speculation length (sv_adaptive_*): `k` is the length for
+    the next round; call update(accepted_mean) after each round."""
+
+    def __init__(self, tiers=(1, 3, 7), beta=0.2, ema0=0.0):
+        L = load()
+        self._s = _AdaptiveState()
+        arr = (ctypes.c_int32 * len(tiers))(*[int(t) for t in tiers])
+        _check(L.sv_adaptive_init(ctypes.byref(self._s), arr, len(tiers), float(beta), float(ema0)))
+
+    @property
+    def k(self) -> int:
+        return int(self._s.k)
+
+    @property
+    def ema(self) -> float:
+        return float(self._s.ema)
+
+    def update(self, accepted_mean) -> int:
+        _check(load().sv_adaptive_update(ctypes.byref(self._s), float(accepted_mean)))
+        return self.k

@@ -680,3 +680,69 @@ int sv_ngram_propose(const int32_t *tokens, int64_t ctx_stride,
 }
 
 } // extern "C"
+
+// ------------------------------------------------------------------ adaptive length
+//
+// [Handbook] "adaptive", the mechanism described for SGLang: after each
+// verification round the mean number of accepted draft tokens per sequence
+// updates an exponential moving average, and the next round's speculation
+// length is one of a few fixed tiers chosen from it.  Host code only.
+
+namespace {
+
+// The smallest tier of at least twice the average, else the largest: as
+// much room above the usual accepted run as the run itself uses.  (The
+// average never exceeds the length in use, so the rule must move up before
+// the average reaches the next tier, and down before it reaches 0.)
+int32_t tier_for(const sv_adaptive &a)
+{
+    for (int32_t i = 0; i < a.ntiers; ++i)
+        if (static_cast<double>(a.tiers[i]) >= 2.0 * a.ema)
+            return a.tiers[i];
+    return a.tiers[a.ntiers - 1];
+}
+
+} // namespace
+
+extern "C" {
+
+int sv_adaptive_init(sv_adaptive *a, const int32_t *tiers, int32_t ntiers, double beta, double ema0)
+{
+    if (!a || !tiers)
+        return fail(SV_ERR_INVALID_ARG, "state and tiers are required");
+    if (ntiers < 1 || ntiers > SV_MAX_TIERS)
+        return fail(SV_ERR_INVALID_ARG, "ntiers = %d outside [1, %d]", ntiers, SV_MAX_TIERS);
+    for (int32_t i = 0; i < ntiers; ++i) {
+        if (tiers[i] < 1 || tiers[i] > SV_MAX_DRAFTS || (i > 0 && tiers[i] <= tiers[i - 1]))
+            return fail(SV_ERR_INVALID_ARG,
+                            "tiers must increase strictly within [1, %d] (tier %d = %d)",
+                            SV_MAX_DRAFTS, i, tiers[i]);
+    }
+    if (!(beta > 0.0 && beta <= 1.0))
+        return fail(SV_ERR_INVALID_ARG, "beta must lie in (0, 1]");
+    if (!(std::isfinite(ema0) && ema0 >= 0.0))
+        return fail(SV_ERR_INVALID_ARG, "ema0 must be finite and >= 0");
+    a->ema = ema0;
+    a->beta = beta;
+    a->ntiers = ntiers;
+    for (int32_t i = 0; i < SV_MAX_TIERS; ++i)
+        a->tiers[i] = i < ntiers ? tiers[i] : 0;
+    a->k = tier_for(*a);
+    return SV_OK;
+}
+
+int sv_adaptive_update(sv_adaptive *a, double accepted_mean)
+{
+    if (!a || a->ntiers < 1 || a->ntiers > SV_MAX_TIERS)
+        return fail(SV_ERR_INVALID_ARG, "state not initialised");
+    if (!(std::isfinite(accepted_mean) && accepted_mean >= 0.0))
+        return fail(SV_ERR_INVALID_ARG, "accepted_mean must be finite and >= 0");
+    {
+#pragma clang fp contract(off)
+        a->ema = (1.0 - a->beta) * a->ema + a->beta * accepted_mean;   // two roundings, as written
+    }
+    a->k = tier_for(*a);
+    return SV_OK;
+}
+
+} // extern "C"

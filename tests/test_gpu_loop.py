@@ -180,3 +180,49 @@ def test_rejection_loop_matches_oracle_loop(orc):
     say("rejection loop: %.2f tokens per step, %d drafts proposed, %d accepted, %d flagged divergences"
         % ((len_h - plen).mean() / steps, proposed, (len_h - plen).sum() - B * steps, flagged))
     assert proposed > B and (len_h - plen).sum() > B * steps + B   # drafts proposed and accepted
+
+
+def test_adaptive_length_loop_stays_lossless():
+    """[Handbook] "adaptive": the speculation length changes between rounds
+    (tiers 1, 3, 7 from the moving average of accepted drafts, read from the
+    verifier's counters), and the output is still plain greedy decoding."""
+    B, rounds, cap, tiers = 128, 40, 1024, (1, 3, 7)
+    table_h = _table(seed=333)
+    rng = np.random.default_rng(33)
+    # prompts that already follow the target (its greedy continuation of a
+    # random start), so lookups hit and the length has a reason to grow
+    prompts = [_plain_greedy(table_h, list(rng.integers(0, V, size=3)), int(n))
+               for n in rng.integers(20, 60, size=B)]
+    plen = np.array([len(q) for q in prompts])
+    d = dev()
+    table = torch.from_numpy(table_h.view(np.int16)).to(d).view(torch.bfloat16)
+    ctx = torch.zeros(B, cap + 8, dtype=torch.int32, device=d)
+    for b, p in enumerate(prompts):
+        ctx[b, :len(p)] = torch.tensor(p, dtype=torch.int32)
+    lengths = torch.tensor(plen, dtype=torch.int32, device=d)
+    ctl = sv.Adaptive(tiers, beta=0.3)
+    used = []
+    say("adaptive loop", B, "sequences", rounds, "rounds")
+    for _ in range(rounds):
+        K = ctl.k
+        used.append(K)
+        prop = sv.ngram_propose(ctx[:, :cap], lengths, 2, 5, K)
+        draft, dlen = prop["proposal"], prop["proposal_len"]
+        L = lengths.long()[:, None]
+        tail = torch.cat([ctx.gather(1, (L - 3 + torch.arange(3, device=d)[None, :])),
+                          draft.clamp(min=0)], dim=1).long()
+        logits = table[_row_index(tail[:, 0:K + 1], tail[:, 1:K + 2], tail[:, 2:K + 3])]
+        stats = torch.zeros(3 + K, dtype=torch.int64, device=d)
+        out = sv.verify_greedy(logits, draft, dlen, stats=stats)
+        acc, emi = out["accepted"].long(), out["emitted"]
+        cols = torch.arange(K + 1, device=d)[None, :]
+        pos = torch.where(cols <= acc[:, None], L + cols, torch.full_like(cols, cap + 7))
+        ctx.scatter_(1, pos, emi)
+        lengths += (acc + 1).int()
+        ctl.update(float(host(stats)[0]) / B)
+    final, ctx_h = host(lengths).astype(np.int64), host(ctx)
+    for b in range(B):
+        ref = _plain_greedy(table_h, prompts[b], int(final[b] - plen[b]))
+        assert list(ctx_h[b, :final[b]]) == ref, "sequence %d diverges" % b
+    say("adaptive loop: lengths used", used)
+    assert len(set(used)) >= 2                      # the length did adapt

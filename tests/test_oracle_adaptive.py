@@ -30,23 +30,36 @@ def test_no_smoothing_follows_the_last_round():
     ks, emas = oracle.adaptive_lengths(acc, beta=1.0, ema0=0.0)
     assert emas == [float(a) for a in acc]
     assert ks == [1] + [oracle.adaptive_tier(a, (1, 3, 7)) for a in acc[:-1]]
+    assert ks == [1, 1, 7, 7, 3, 7, 7]
 
 
 def test_tier_rule():
-    """The smallest tier strictly above the average, else the largest: a
-    tier, non-decreasing in the average, and never below it unless the
-    largest tier is."""
+    """The smallest tier of at least twice the average, else the largest:
+    a tier, non-decreasing in the average, never below twice the average
+    unless the largest tier is, and the tier below it always is."""
     tiers = (1, 3, 7)
     prev = 0
     for e in np.linspace(0.0, 10.0, 1001):
         k = oracle.adaptive_tier(e, tiers)
         assert k in tiers and k >= prev
         prev = k
-        if e < tiers[-1]:
-            assert k > e and all(t <= e for t in tiers if t < k)
+        if 2.0 * e <= tiers[-1]:
+            assert k >= 2.0 * e and all(t < 2.0 * e for t in tiers if t < k)
         else:
             assert k == tiers[-1]
-    assert oracle.adaptive_tier(2.999, tiers) == 3 and oracle.adaptive_tier(3.0, tiers) == 7
+    assert oracle.adaptive_tier(0.5, tiers) == 1 and oracle.adaptive_tier(0.51, tiers) == 3
+    assert oracle.adaptive_tier(1.5, tiers) == 3 and oracle.adaptive_tier(1.51, tiers) == 7
+
+
+def test_moves_both_ways_from_the_ends():
+    """At length 1 the average never exceeds 1, yet drafts accepted 60% of
+    the time move the length up; under sustained full rejection the average
+    only approaches 0, yet the length comes back down to 1."""
+    ks, emas = oracle.adaptive_lengths([0.6] * 20, ema0=0.0)
+    assert ks[0] == 1 and ks[-1] == 3
+    assert all(k == oracle.adaptive_tier(e, (1, 3, 7)) for k, e in zip(ks[1:], emas))
+    ks, _ = oracle.adaptive_lengths([0.0] * 20, ema0=7.0)
+    assert ks[0] == 7 and ks[-1] == 1
 
 
 def test_converges_to_the_matching_tier():
