@@ -607,6 +607,15 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     }
     p.inv_t_d = 1.0 / static_cast<double>(temperature);
     p.inv_t = static_cast<float>(p.inv_t_d);
+    {
+        const double c = 1.4426950408889634 / static_cast<double>(temperature);   // log2(e) / T
+        int ex = 0;
+        const double m = std::frexp(c, &ex);                      // c = m 2^ex, m in [0.5, 1)
+        const double c1 = std::ldexp(std::nearbyint(std::ldexp(m, 16)), ex - 16);
+        p.split_c1 = static_cast<float>(c1);                      // exact: 16 significant bits
+        p.split_k2 = static_cast<float>((c - c1) * 0.69314718055994531);
+        p.split_ok = c >= 0x1p-60 && c <= 0x1p60;
+    }
     p.draft = K > 0 ? draft : accepted;
     p.draft_len = draft_len ? draft_len : accepted;
     p.has_len = draft_len != nullptr;

@@ -6,8 +6,11 @@
 // target rows and K draft rows of every sequence streams the logits once
 // with 16-byte loads (the pieces are sized so that every wave of the launch
 // is resident at once).  Each lane sums exp(l / T) against the fixed
-// reference 0 with the compensated hardware exp2 (about one ulp): fp32 sums
-// of 8 terms, fp64 across them.  The rare vectors whose fp32 sum leaves a
+// reference 0 (fp32 sums of 8 terms, fp64 across them).  For bf16 logits
+// the hardware exp2 takes the exact product of l and log2(e)/T rounded to
+// 16 bits, and the rounding is corrected to first order through a second
+// sum, of the terms weighted by l; fp32 logits use the compensated exp
+// (about one ulp either way).  The rare vectors whose fp32 sum leaves a
 // wide range (logits above about 44 T, -inf entries, rows far below 0) go
 // through a careful path with its own reference and fp64 rescales.  The
 // wave combines its lanes onto their largest reference and writes
@@ -114,14 +117,50 @@ __device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSu
     }
 }
 
+// How the fast path forms e^(l/T).
+enum ExpMode : int {
+    kExpUnitT = 0,    // compensated exp of l (T == 1)
+    kExpScaled = 1,   // compensated exp of l * (1/T)
+    kExpSplit = 2,    // bf16 only: split constant, first-order correction summed apart
+};
+
+// Sum of e^(f_j / T) over a vector, in fp32.  kExpSplit: with log2(e)/T =
+// c1 + c2, c1 of 16 significant bits, y = f c1 is exact for bf16 f, and
+// e^(f/T) = 2^y 2^(f c2) = 2^y (1 + f c2 ln 2 + ...), so the vector's sum is
+// s1 + k2 s2 with s1 = sum of 2^y, s2 = sum of 2^y f and k2 = c2 ln 2.  The
+// dropped terms are below (|y| 2^-16 ln 2)^2 / 2 relative: under 2.3e-7
+// for the |y| <= 64 that an in-range sum allows, about 1e-9 at |y| <= 10.
+template <int kMode, int n>
+__device__ __forceinline__ float vec_exp_sum(const float (&f)[n], float inv_t, float c1, float k2)
+{
+    if constexpr (kMode == kExpSplit) {
+        float e = __builtin_amdgcn_exp2f(f[0] * c1);
+        float s1 = e, s2 = e * f[0];
+#pragma unroll
+        for (int j = 1; j < n; ++j) {
+            e = __builtin_amdgcn_exp2f(f[j] * c1);
+            s1 += e;
+            s2 = __builtin_fmaf(e, f[j], s2);
+        }
+        return __builtin_fmaf(k2, s2, s1);
+    } else {
+        float s = exp_c(kMode == kExpUnitT ? f[0] : f[0] * inv_t);
+#pragma unroll
+        for (int j = 1; j < n; ++j)
+            s += exp_c(kMode == kExpUnitT ? f[j] : f[j] * inv_t);
+        return s;
+    }
+}
+
 // One wave per work item (row, piece); a workgroup carries four items.
 // The partial's reference is at most about e^44 below every element of the
 // piece (fast-path vectors sum to at most 2^64 against 0; careful vectors
 // are taken against their own maximum) and, when the piece has terms of
 // non-negligible size against 0, at least 0.
-template <typename E, bool kUnitT>
+template <typename E, int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_stats(const RejectParams p)
 {
+    constexpr bool kUnitT = kMode == kExpUnitT;
     const int lane = threadIdx.x & 63;
     const int K = p.K;
     const int rows_per_seq = 2 * K + 1;
@@ -147,27 +186,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const int hi = min(p.V, lo + p.seg_len);
         const float inv_t = p.inv_t;
         const double inv_t_d = p.inv_t_d;
-        auto arg = [&](float x) { return kUnitT ? x : x * inv_t; };
+        const float c1 = p.split_c1, k2 = p.split_k2;
         stream_segment<E, 4, 64>(
             rp, lo, hi, lane,
             [&](const float(&f)[Elem<E>::kPerVec], int) {
-                constexpr int PV = Elem<E>::kPerVec;
-                float s = exp_c(arg(f[0]));
-#pragma unroll
-                for (int j = 1; j < PV; ++j)
-                    s += exp_c(arg(f[j]));
+                const float s = vec_exp_sum<kMode>(f, inv_t, c1, k2);
                 if (s >= kTiny && s <= kBig)
                     ls.z0 += static_cast<double>(s);
                 else
                     careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
             },
             [&](float x, int) {
-                const float s = exp_c(arg(x));
+                const float f1[1] = {x};
+                const float s = vec_exp_sum<kMode>(f1, inv_t, c1, k2);
                 if (s >= kTiny && s <= kBig) {
                     ls.z0 += static_cast<double>(s);
                 } else {
-                    const float f[1] = {x};
-                    careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
+                    careful_add<kUnitT>(f1, s, ls, inv_t, inv_t_d);
                 }
             });
     }
@@ -659,10 +694,12 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
 {
     const int64_t items = static_cast<int64_t>(p.B) * (2 * p.K + 1) * p.segs;
     const dim3 g1(static_cast<unsigned>((items + kWaves - 1) / kWaves));
-    if (p.inv_t == 1.0f)
-        hipLaunchKernelGGL((k_rej_stats<E, true>), g1, dim3(kThreads), 0, s, p);
+    if (sizeof(E) == 2 && p.split_ok)
+        hipLaunchKernelGGL((k_rej_stats<E, kExpSplit>), g1, dim3(kThreads), 0, s, p);
+    else if (p.inv_t == 1.0f)
+        hipLaunchKernelGGL((k_rej_stats<E, kExpUnitT>), g1, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_rej_stats<E, false>), g1, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_rej_stats<E, kExpScaled>), g1, dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

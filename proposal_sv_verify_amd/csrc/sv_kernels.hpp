@@ -99,6 +99,13 @@ struct RejectParams {
                               // the elements per vector
     float inv_t;
     double inv_t_d;
+    // log2(e) / T = split_c1 + split_c2 with split_c1 rounded to 16
+    // significant bits, so that a bf16 logit (8 significant bits) times
+    // split_c1 is exact in fp32; split_k2 = split_c2 * ln 2 in fp32.
+    // split_ok: split_c1 lies far from fp32's range ends.
+    float split_c1;
+    float split_k2;
+    int32_t split_ok;
     // draft, draftl and draft_len always point at valid memory, so kernels can
     // load from them unconditionally: with K == 0 draft and draftl stand in
     // for nothing (any int array, the target logits), and without lengths
