@@ -156,6 +156,68 @@ def ngram_bandwidth_mode(args):
                 gb_per_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
 
 
+def _timed(fns, reps):
+    """HIP-event mean of one pass over fns, over reps passes (after 3)."""
+    import torch
+    for _ in range(3):
+        for f in fns:
+            f()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        for f in fns:
+            f()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+
+def rejection_shards(d, shards=8, reps=30):
+    """The rejection workload in the eight 16032-column vocabulary shards
+    of an 8-way tensor-parallel output layer: per-shard statistics, the
+    accept test on the partials, per-shard sample masses and the owner
+    shard's sample, beside the unsharded call.  HIP-event means."""
+    import torch
+    import proposal_sv_verify_amd as sv
+
+    tg, dg, x, u = d["rj_t"], d["rj_d"], d["rj_x"], d["rj_u"]
+    B, K1, V = tg.shape
+    K = K1 - 1
+    dev = tg.device
+    cuts = [(i * V // shards, (i + 1) * V // shards) for i in range(shards)]
+    parts = torch.empty(shards, B * (2 * K + 1), 2, dtype=torch.float64, device=dev)
+    stats_calls = [sv.prepare_rejection_shard_stats(tg[..., a:b], dg[..., a:b], x, a, 1.0,
+                                                    out=parts[p]) for p, (a, b) in enumerate(cuts)]
+    for c in stats_calls:
+        c()
+    decide = sv.prepare_rejection_partials(parts, x, u, V, 1.0)
+    state = decide()["state"]
+    masses = torch.empty(shards, B, 2, dtype=torch.float64, device=dev)
+    mass_calls = [sv.prepare_rejection_shard_mass(tg[..., a:b], dg[..., a:b], state, 1.0,
+                                                  out=masses[p]) for p, (a, b) in enumerate(cuts)]
+    emitted = torch.full((B, K1), -1, dtype=torch.int32, device=dev)
+    sample_calls = [sv.prepare_rejection_shard_sample(tg[..., a:b], dg[..., a:b], x, u, state, masses,
+                                                      p, a, mass_calls[p].out["workspace"], emitted,
+                                                      1.0) for p, (a, b) in enumerate(cuts)]
+    whole = sv.prepare_rejection(tg, dg, x, u, 1.0)
+    t_stats = _timed(stats_calls, reps)
+    t_decide = _timed([decide], reps)
+    t_mass = _timed(mass_calls, reps)
+    t_sample = _timed(sample_calls, reps)
+    t_all = _timed(stats_calls + [decide] + mass_calls + sample_calls, reps)
+    t_whole = _timed([whole], reps)
+    ref = whole()
+    same_acc = int((decide()["accepted"] == ref["accepted"]).sum())
+    same_emi = int((emitted == ref["emitted"]).all(dim=1).sum())
+    nbytes = B * (2 * K + 1) * V * 2
+    return dict(shards=shards, us_stats_calls=round(t_stats, 2), us_accept=round(t_decide, 2),
+                us_mass_calls=round(t_mass, 2), us_sample_calls=round(t_sample, 2),
+                us_all_steps=round(t_all, 2), us_unsharded=round(t_whole, 2),
+                gb_per_s_stats_calls=round(nbytes / t_stats / 1e3, 1),
+                sequences_same_accepted=same_acc, sequences_same_emitted=same_emi, sequences=B)
+
+
 def greedy_shards(gr, shards=8, reps=30):
     """The large greedy workload as an 8-way vocabulary-sharded output layer
     would hold it: sv_argmax_shard on each 18992-column slice, then
@@ -175,23 +237,9 @@ def greedy_shards(gr, shards=8, reps=30):
     combine = sv.prepare_greedy_partials(parts, dr, V)
     whole = sv.prepare_greedy(lg, dr)
 
-    def timed(fns):
-        for _ in range(3):
-            for f in fns:
-                f()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record()
-        for _ in range(reps):
-            for f in fns:
-                f()
-        ev[1].record()
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
-
-    t_shards = timed(shard_calls)
-    t_combine = timed([combine])
-    t_whole = timed([whole])
+    t_shards = _timed(shard_calls, reps)
+    t_combine = _timed([combine], reps)
+    t_whole = _timed([whole], reps)
     same = all(torch.equal(combine()[k], whole()[k]) for k in ("accepted", "emitted", "argmax"))
     nbytes = rows * V * 2
     return dict(shards=shards, us_shard_calls=round(t_shards, 2), us_combine=round(t_combine, 2),
@@ -298,7 +346,7 @@ def main():
     ap.add_argument("--no-bandwidth-mode", action="store_true",
                     help="skip the 16384-context n-gram measurement")
     ap.add_argument("--no-shards", action="store_true",
-                    help="skip the vocabulary-sharded greedy measurement")
+                    help="skip the vocabulary-sharded greedy and rejection measurements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy a 256 MiB device buffer three times (a "
                          "kernel of known traffic for scaling the rocprofv3 byte counters)")
@@ -309,7 +357,7 @@ def main():
         sys.exit(2)
 
     ng, rj, gr, tr = make_inputs()
-    wall, samples, outs, _ = run_gpu(args, ng, rj, gr, tr)
+    wall, samples, outs, dev_inputs = run_gpu(args, ng, rj, gr, tr)
     per = {name: float(np.mean(v)) for name, v in samples.items()}
     if args.calibrate_copy:
         calibrate_copy()
@@ -356,6 +404,7 @@ def main():
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
     if not args.no_shards:
         result["greedy_vocab_shards"] = greedy_shards(gr)
+        result["rejection_vocab_shards"] = rejection_shards(dev_inputs)
     if not args.no_cpu:
         cb, parity = cpu_baseline(ng, rj, gr, tr, args.cpu_seconds, outs)
         result["cpu_baseline"] = cb

@@ -258,6 +258,94 @@ int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
                             int32_t *argmax_out, uint32_t *flags, void *stream);
 
 /*
+ * Vocabulary-sharded rejection sampling: sv_verify_rejection split into
+ * four steps with three small exchanges between them ([Arctic] "inference
+ * pipeline optimisation" reduces sharded logits per shard before gathering;
+ * here the per-shard reductions are softmax statistics and sample masses).
+ * Shard s holds the columns [v_offset_s, v_offset_s + V_s) of every target
+ * and draft row; the shards must cover [0, V) once.
+ *
+ * 1. sv_rejection_shard_stats (per shard): for every row of the sequence's
+ *    K+1 target and K draft rows (row order: target rows 0..K, then draft
+ *    rows 0..K-1; out[b * (2K+1) + r]): z = sum over the shard's columns of
+ *    exp((l - m) / T) against the reference m (a row with nothing above
+ *    -inf, or a row past draft_len that the call skips, gives z = 0,
+ *    m = -inf), and lx = the row's logit at its draft token x_i (target
+ *    row i < K and draft row i) when x_i lies in the shard, else NaN.
+ *    Arguments as for sv_verify_rejection, with V the shard's width; out
+ *    [B][2K+1] sv_softmax_partial (8-byte aligned); workspace as sized by
+ *    sv_rejection_shard_workspace_bytes(B, K, V).
+ * 2. sv_verify_rejection_partials (once, on every shard's partials):
+ *    partials [P][B][2K+1], shard p's row r at partials[p * B*(2K+1) + r];
+ *    V the full vocabulary.  Merges each row's shards, then runs the accept
+ *    test exactly as sv_verify_rejection: writes accepted, p_draft,
+ *    q_draft, flags and stats as it does, and state[b] for the steps below.
+ * 3. sv_rejection_shard_mass (per shard): out[b] = the shard's sum of
+ *    r = max(0, p_n - q_n) (the residual; 0 when every draft was accepted)
+ *    and of p_n, over its columns of row pair n = state[b].n.
+ * 4. sv_rejection_shard_sample (per shard, the same workspace as its step
+ *    3, unchanged since): masses [P][B] of every shard (shard p's at
+ *    masses[p * B + b]).  S = the sum over shards in shard order of the
+ *    residual masses (of p_n when every draft was accepted or the residual
+ *    sums to 0); the shard where the running sum first exceeds u[b][K] * S
+ *    (else the last shard with mass) owns the sample.  Only the owner's
+ *    call writes emitted[b] (as sv_verify_rejection would), so after the
+ *    calls of all P shards every sequence is written once.
+ * Decisions and samples agree with sv_verify_rejection on the concatenated
+ * logits except within the rounding band of a tie (sums are associated by
+ * shard).  Limits: 1 <= P <= SV_MAX_REJECT_SHARDS, 0 <= v_offset,
+ * v_offset + V <= SV_MAX_V, and those of sv_verify_rejection.
+ */
+typedef struct {
+    double z;          /* sum of exp((l - m) / T) over the shard's columns */
+    float m;           /* reference of z */
+    float lx;          /* logit at the row's draft token, or NaN */
+} sv_softmax_partial;
+
+typedef struct {
+    double zt, zd;     /* normalisers of target row n and draft row n */
+    float mt, md;      /* their references: p_n(v) = exp((l - mt) / T) / zt */
+    int32_t n;         /* accepted drafts */
+    int32_t len;       /* draft length used (n < len: residual sample) */
+} sv_rejection_state;
+
+typedef struct {
+    double r;          /* sum of max(0, p_n - q_n) */
+    double p;          /* sum of p_n */
+} sv_sample_mass;
+
+#define SV_MAX_REJECT_SHARDS 16
+
+size_t sv_rejection_shard_workspace_bytes(int32_t B, int32_t K, int32_t V);
+int sv_rejection_shard_stats(const void *target_logits, const void *draft_logits,
+                             int32_t dtype, int64_t row_stride,
+                             const int32_t *draft, const int32_t *draft_len, float temperature,
+                             int32_t B, int32_t K, int32_t V, int32_t v_offset,
+                             sv_softmax_partial *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+int sv_verify_rejection_partials(const sv_softmax_partial *partials, int32_t P,
+                                 const int32_t *draft, const int32_t *draft_len,
+                                 const float *uniforms, float temperature,
+                                 int32_t B, int32_t K, int32_t V,
+                                 int32_t *accepted, float *p_draft, float *q_draft,
+                                 uint32_t *flags, int64_t *stats,
+                                 sv_rejection_state *state, void *stream);
+int sv_rejection_shard_mass(const void *target_logits, const void *draft_logits,
+                            int32_t dtype, int64_t row_stride,
+                            const sv_rejection_state *state, float temperature,
+                            int32_t B, int32_t K, int32_t V,
+                            sv_sample_mass *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+int sv_rejection_shard_sample(const void *target_logits, const void *draft_logits,
+                              int32_t dtype, int64_t row_stride,
+                              const int32_t *draft, const float *uniforms,
+                              const sv_rejection_state *state,
+                              const sv_sample_mass *masses, int32_t P, int32_t shard,
+                              float temperature, int32_t B, int32_t K, int32_t V, int32_t v_offset,
+                              int32_t *emitted,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Adaptive speculation length -- [Handbook] "adaptive" (the mechanism it
  * describes for SGLang): after each verification round, the mean number of
  * accepted draft tokens per sequence updates an exponential moving average,

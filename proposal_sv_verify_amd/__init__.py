@@ -36,6 +36,8 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_se
            "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose",
            "sv_argmax_shard_workspace_bytes", "sv_argmax_shard",
            "sv_verify_greedy_partials", "sv_verify_tree_partials",
+           "sv_rejection_shard_workspace_bytes", "sv_rejection_shard_stats",
+           "sv_verify_rejection_partials", "sv_rejection_shard_mass", "sv_rejection_shard_sample",
            "sv_adaptive_init", "sv_adaptive_update")
 
 # One sv_argmax_partial: the row's largest value and the lowest global token
@@ -43,6 +45,15 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_se
 # keeps partials in int64 tensors, one element per partial.
 PARTIAL_DTYPE = np.dtype([("value", "<f4"), ("index", "<i4")])
 NO_INDEX = 0x7FFFFFFF
+
+# Sharded rejection sampling: sv_softmax_partial, sv_rejection_state and
+# sv_sample_mass records, kept in float64 tensors of 2, 4 and 2 elements per
+# record.
+SOFT_PARTIAL_DTYPE = np.dtype([("z", "<f8"), ("m", "<f4"), ("lx", "<f4")])
+STATE_DTYPE = np.dtype([("zt", "<f8"), ("zd", "<f8"), ("mt", "<f4"), ("md", "<f4"),
+                        ("n", "<i4"), ("len", "<i4")])
+MASS_DTYPE = np.dtype([("r", "<f8"), ("p", "<f8")])
+MAX_REJECT_SHARDS = 16
 
 
 class SpecVerifyError(RuntimeError):
@@ -96,6 +107,20 @@ def load(path: str = LIB_PATH):
         L.sv_argmax_shard.argtypes = [P, i32, i64, i32, i32, i32, P, P, sz, P]
         L.sv_verify_greedy_partials.restype = ctypes.c_int
         L.sv_verify_greedy_partials.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P, P, P]
+        L.sv_rejection_shard_workspace_bytes.restype = sz
+        L.sv_rejection_shard_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_rejection_shard_stats.restype = ctypes.c_int
+        L.sv_rejection_shard_stats.argtypes = [P, P, i32, i64, P, P, ctypes.c_float, i32, i32, i32,
+                                               i32, P, P, sz, P]
+        L.sv_verify_rejection_partials.restype = ctypes.c_int
+        L.sv_verify_rejection_partials.argtypes = [P, i32, P, P, P, ctypes.c_float, i32, i32, i32,
+                                                   P, P, P, P, P, P, P]
+        L.sv_rejection_shard_mass.restype = ctypes.c_int
+        L.sv_rejection_shard_mass.argtypes = [P, P, i32, i64, P, ctypes.c_float, i32, i32, i32, P,
+                                              P, sz, P]
+        L.sv_rejection_shard_sample.restype = ctypes.c_int
+        L.sv_rejection_shard_sample.argtypes = [P, P, i32, i64, P, P, P, P, i32, i32, ctypes.c_float,
+                                                i32, i32, i32, i32, P, P, sz, P]
         L.sv_adaptive_init.restype = ctypes.c_int
         L.sv_adaptive_init.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
         L.sv_adaptive_update.restype = ctypes.c_int
@@ -424,6 +449,153 @@ def prepare_tree_partials(partials, parent, token, V, *, want_argmax=True):
 
 def verify_tree_partials(*a, **k):
     return prepare_tree_partials(*a, **k)()
+
+
+def _shard_logits(target, draft_logits):
+    """Validate a shard's target [B, K+1, Vs] and draft [B, K, Vs] column
+    slices; returns (dtype code, row stride, B, K, Vs)."""
+    code, rs = _logits_args(target, "target", 2)
+    B, K1, Vs = target.shape
+    K = K1 - 1
+    if K > 0:
+        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2)
+        if code2 != code or rs2 != rs or tuple(draft_logits.shape) != (B, K, Vs):
+            raise ValueError("draft_logits must be [B, K, Vs] with the target's dtype and row stride")
+    return code, rs, B, K, Vs
+
+
+def _f64_records(t, shape, name):
+    torch = _torch()
+    if t.dtype != torch.float64 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be a contiguous float64 tensor of shape %s" % (name, tuple(shape)))
+    return t
+
+
+def prepare_rejection_shard_stats(target, draft_logits, draft, v_offset, temperature=1.0,
+                                  draft_len=None, out=None):
+    """Step 1 of sharded rejection sampling, for one shard: target [B, K+1,
+    Vs] and draft_logits [B, K, Vs] are the shard's column slices, v_offset
+    its first global id.  Output: partial, float64 [B*(2K+1), 2] (one
+    sv_softmax_partial per row; decode with SOFT_PARTIAL_DTYPE); pass `out`
+    (e.g. one row of a [P, B*(2K+1), 2] tensor) to write in place."""
+    torch = _torch()
+    L = load()
+    code, rs, B, K, Vs = _shard_logits(target, draft_logits)
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    rows = B * (2 * K + 1)
+    dev = target.device
+    if out is None:
+        out = torch.empty(rows, 2, dtype=torch.float64, device=dev)
+    _f64_records(out, (rows, 2), "out")
+    s = _stream(dev)
+    ws = workspace(L.sv_rejection_shard_workspace_bytes(B, K, Vs), dev, s)
+    args = (target.data_ptr(), _ptr(draft_logits) if K > 0 else None, code, rs, _ptr(draft),
+            _ptr(draft_len), float(temperature), B, K, Vs, int(v_offset), out.data_ptr(),
+            ws.data_ptr(), ws.numel(), s)
+    return Prepared(L.sv_rejection_shard_stats, args, dict(partial=out),
+                    (target, draft_logits, draft, draft_len, out, ws))
+
+
+def rejection_shard_stats(*a, **k):
+    return prepare_rejection_shard_stats(*a, **k)()
+
+
+def prepare_rejection_partials(partials, draft, uniforms, V, temperature=1.0, draft_len=None, *,
+                               want_probs=True, stats=None):
+    """Step 2: the accept test on every shard's partials [P, B*(2K+1), 2]
+    (float64), draft [B, K], uniforms [B, K+1], V = the full vocabulary.
+    Outputs: accepted, p_draft, q_draft, flags as prepare_rejection, and
+    state, float64 [B, 4] (one sv_rejection_state per sequence; decode with
+    STATE_DTYPE) for steps 3 and 4."""
+    torch = _torch()
+    L = load()
+    B, K = draft.shape
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    if partials.dim() != 3:
+        raise ValueError("partials must be [P, B*(2K+1), 2]")
+    Pn = partials.shape[0]
+    _f64_records(partials, (Pn, B * (2 * K + 1), 2), "partials")
+    if uniforms.dtype != torch.float32 or not uniforms.is_contiguous() or \
+            tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("uniforms must be a contiguous float32 tensor [B, K+1]")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 3 + K):
+        raise ValueError("stats must be an int64 tensor of at least 3+K entries")
+    dev = partials.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    pd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    qd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    state = torch.empty(B, 4, dtype=torch.float64, device=dev)
+    args = (partials.data_ptr(), Pn, _ptr(draft), _ptr(draft_len), uniforms.data_ptr(),
+            float(temperature), B, K, int(V), acc.data_ptr(), _ptr(pd), _ptr(qd), flg.data_ptr(),
+            _ptr(stats), state.data_ptr(), _stream(dev))
+    out = dict(accepted=acc, flags=flg, state=state)
+    if want_probs:
+        out["p_draft"], out["q_draft"] = pd, qd
+    return Prepared(L.sv_verify_rejection_partials, args, out,
+                    (partials, draft, draft_len, uniforms, stats))
+
+
+def verify_rejection_partials(*a, **k):
+    return prepare_rejection_partials(*a, **k)()
+
+
+def prepare_rejection_shard_mass(target, draft_logits, state, temperature=1.0, out=None):
+    """Step 3, for one shard: the shard's final-sample masses out [B, 2]
+    (float64; one sv_sample_mass per sequence, decode with MASS_DTYPE).
+    The call gets a workspace of its own, returned as `workspace`: step 4
+    of the same shard takes it back."""
+    torch = _torch()
+    L = load()
+    code, rs, B, K, Vs = _shard_logits(target, draft_logits)
+    _f64_records(state, (B, 4), "state")
+    dev = target.device
+    if out is None:
+        out = torch.empty(B, 2, dtype=torch.float64, device=dev)
+    _f64_records(out, (B, 2), "out")
+    ws = torch.empty(max(256, L.sv_rejection_shard_workspace_bytes(B, K, Vs)), dtype=torch.uint8,
+                     device=dev)
+    args = (target.data_ptr(), _ptr(draft_logits) if K > 0 else None, code, rs, state.data_ptr(),
+            float(temperature), B, K, Vs, out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    return Prepared(L.sv_rejection_shard_mass, args, dict(mass=out, workspace=ws),
+                    (target, draft_logits, state, out, ws))
+
+
+def rejection_shard_mass(*a, **k):
+    return prepare_rejection_shard_mass(*a, **k)()
+
+
+def prepare_rejection_shard_sample(target, draft_logits, draft, uniforms, state, masses, shard,
+                                   v_offset, workspace, emitted, temperature=1.0):
+    """Step 4, for one shard: masses [P, B, 2] float64 of every shard,
+    `workspace` the one step 3 returned for this shard, emitted [B, K+1]
+    int32 written in place for the sequences whose sample this shard owns."""
+    torch = _torch()
+    L = load()
+    code, rs, B, K, Vs = _shard_logits(target, draft_logits)
+    _i32(draft, (B, K), "draft")
+    _i32(emitted, (B, K + 1), "emitted")
+    _f64_records(state, (B, 4), "state")
+    if masses.dim() != 3:
+        raise ValueError("masses must be [P, B, 2]")
+    Pn = masses.shape[0]
+    _f64_records(masses, (Pn, B, 2), "masses")
+    if uniforms.dtype != torch.float32 or not uniforms.is_contiguous() or \
+            tuple(uniforms.shape) != (B, K + 1):
+        raise ValueError("uniforms must be a contiguous float32 tensor [B, K+1]")
+    dev = target.device
+    args = (target.data_ptr(), _ptr(draft_logits) if K > 0 else None, code, rs, _ptr(draft),
+            uniforms.data_ptr(), state.data_ptr(), masses.data_ptr(), Pn, int(shard),
+            float(temperature), B, K, Vs, int(v_offset), emitted.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), _stream(dev))
+    return Prepared(L.sv_rejection_shard_sample, args, dict(emitted=emitted),
+                    (target, draft_logits, draft, uniforms, state, masses, workspace, emitted))
+
+
+def rejection_shard_sample(*a, **k):
+    return prepare_rejection_shard_sample(*a, **k)()
 
 
 # ---------------------------------------------------------------- adaptive length

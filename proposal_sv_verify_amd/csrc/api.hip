@@ -541,6 +541,50 @@ int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
 
 // ------------------------------------------------------------------ rejection
 
+namespace {
+
+// Temperature constants of a rejection-sampling launch: 1/T in fp32 and
+// fp64, and log2(e)/T split into a 16-bit head and a remainder times ln 2
+// (the bf16 statistics kernel's exact-product exp).
+void set_temperature(sv::RejectParams &p, float temperature)
+{
+    p.inv_t_d = 1.0 / static_cast<double>(temperature);
+    p.inv_t = static_cast<float>(p.inv_t_d);
+    const double c = 1.4426950408889634 / static_cast<double>(temperature);   // log2(e) / T
+    int ex = 0;
+    const double m = std::frexp(c, &ex);                      // c = m 2^ex, m in [0.5, 1)
+    const double c1 = std::ldexp(std::nearbyint(std::ldexp(m, 16)), ex - 16);
+    p.split_c1 = static_cast<float>(c1);                      // exact: 16 significant bits
+    p.split_k2 = static_cast<float>((c - c1) * 0.69314718055994531);
+    p.split_ok = c >= 0x1p-60 && c <= 0x1p60;
+}
+
+// Logit rows of one call (all rows, or one vocabulary shard's columns).
+void set_rows(sv::RejectParams &p, const void *target_logits, const void *draft_logits, int dtype,
+              int64_t row_stride, int32_t B, int32_t K, int32_t V)
+{
+    p.target = target_logits;
+    p.draftl = K > 0 ? draft_logits : target_logits;
+    p.row_stride = row_stride;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.v_full = V;
+    p.nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
+    const int64_t esize = esize_of(dtype);
+    p.vec_ok = !misaligned(target_logits, 16) && (K == 0 || !misaligned(draft_logits, 16)) &&
+               (row_stride * esize) % 16 == 0 && V % (16 / esize) == 0;
+}
+
+int check_temperature(float temperature)
+{
+    if (!(std::isfinite(temperature) && temperature > 0.0f))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    return SV_OK;
+}
+
+} // namespace
+
 size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V)
 {
     if (B < 1 || K < 0 || V < 1)
@@ -573,8 +617,8 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
         return fail(SV_ERR_INVALID_ARG, "draft is NULL");
     if (!uniforms)
         return fail(SV_ERR_INVALID_ARG, "uniforms is NULL");
-    if (!(std::isfinite(temperature) && temperature > 0.0f))
-        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if ((st = check_temperature(temperature)) != SV_OK)
+        return st;
     if (!accepted || !emitted)
         return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
@@ -591,31 +635,12 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
         return st;
 
     sv::RejectParams p{};
-    p.target = target_logits;
-    p.draftl = K > 0 ? draft_logits : target_logits;
-    p.row_stride = row_stride;
-    p.B = B;
-    p.K = K;
-    p.V = V;
+    set_rows(p, target_logits, draft_logits, dtype, row_stride, B, K, V);
     p.segs = pl.segs;
     p.seg_len = pl.seg_len;
-    p.nchunks = nchunks;
-    {
-        const int64_t esize = esize_of(dtype);
-        p.vec_ok = !misaligned(target_logits, 16) && (K == 0 || !misaligned(draft_logits, 16)) &&
-                   (row_stride * esize) % 16 == 0 && V % (16 / esize) == 0;
-    }
-    p.inv_t_d = 1.0 / static_cast<double>(temperature);
-    p.inv_t = static_cast<float>(p.inv_t_d);
-    {
-        const double c = 1.4426950408889634 / static_cast<double>(temperature);   // log2(e) / T
-        int ex = 0;
-        const double m = std::frexp(c, &ex);                      // c = m 2^ex, m in [0.5, 1)
-        const double c1 = std::ldexp(std::nearbyint(std::ldexp(m, 16)), ex - 16);
-        p.split_c1 = static_cast<float>(c1);                      // exact: 16 significant bits
-        p.split_k2 = static_cast<float>((c - c1) * 0.69314718055994531);
-        p.split_ok = c >= 0x1p-60 && c <= 0x1p60;
-    }
+    p.part_row_step = pl.segs;
+    p.part_seg_step = 1;
+    set_temperature(p, temperature);
     p.draft = K > 0 ? draft : accepted;
     p.draft_len = draft_len ? draft_len : accepted;
     p.has_len = draft_len != nullptr;
@@ -632,6 +657,234 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     hipError_t e = sv::launch_rejection(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "rejection launch");
+    return SV_OK;
+}
+
+// ------------------------------------------------------- rejection, sharded
+
+static_assert(sizeof(sv_softmax_partial) == sizeof(sv::SoftPartial), "partial layout");
+static_assert(sizeof(sv_rejection_state) == sizeof(sv::SeqState), "state layout");
+static_assert(sizeof(sv_sample_mass) == sizeof(sv::ChunkMass), "mass layout");
+static_assert(SV_MAX_REJECT_SHARDS <= sv::kMaxSegs, "shards merge like row segments");
+
+namespace {
+
+int check_shard_rows(const void *target_logits, const void *draft_logits, int32_t dtype,
+                     int64_t row_stride, int32_t B, int32_t K, int32_t V, int32_t v_offset)
+{
+    int st;
+    if ((st = check_sizes(B, K, V)) != SV_OK)
+        return st;
+    if (v_offset < 0)
+        return fail(SV_ERR_INVALID_ARG, "v_offset = %d < 0", v_offset);
+    if (static_cast<int64_t>(v_offset) + V > SV_MAX_V)
+        return fail(SV_ERR_UNSUPPORTED, "v_offset + V = %lld above %d",
+                    static_cast<long long>(v_offset) + V, SV_MAX_V);
+    if ((st = check_logits(target_logits, dtype, row_stride, V, "target_logits")) != SV_OK)
+        return st;
+    if (K > 0 && (st = check_logits(draft_logits, dtype, row_stride, V, "draft_logits")) != SV_OK)
+        return st;
+    return SV_OK;
+}
+
+int check_shard_count(int32_t P)
+{
+    if (P < 1)
+        return fail(SV_ERR_INVALID_ARG, "P = %d < 1", P);
+    if (P > SV_MAX_REJECT_SHARDS)
+        return fail(SV_ERR_UNSUPPORTED, "P = %d above %d", P, SV_MAX_REJECT_SHARDS);
+    return SV_OK;
+}
+
+} // namespace
+
+size_t sv_rejection_shard_workspace_bytes(int32_t B, int32_t K, int32_t V)
+{
+    return sv_rejection_workspace_bytes(B, K, V);
+}
+
+int sv_rejection_shard_stats(const void *target_logits, const void *draft_logits,
+                             int32_t dtype, int64_t row_stride,
+                             const int32_t *draft, const int32_t *draft_len, float temperature,
+                             int32_t B, int32_t K, int32_t V, int32_t v_offset,
+                             sv_softmax_partial *out,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if ((st = check_shard_rows(target_logits, draft_logits, dtype, row_stride, B, K, V, v_offset)) != SV_OK)
+        return st;
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if ((st = check_temperature(temperature)) != SV_OK)
+        return st;
+    if (!out || misaligned(out, 8))
+        return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
+    const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
+    const RowPlan pl = plan_items(rows, V, esize_of(dtype));
+    const RejLayout L = rej_layout(B, K, V, pl);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    if ((st = check_grid((rows * pl.segs + 3) / 4)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::RejectParams p{};
+    set_rows(p, target_logits, draft_logits, dtype, row_stride, B, K, V);
+    p.segs = pl.segs;
+    p.seg_len = pl.seg_len;
+    set_temperature(p, temperature);
+    p.v_offset = v_offset;
+    p.capture_x = 1;
+    p.draft = K > 0 ? draft : reinterpret_cast<const int32_t *>(out);
+    p.draft_len = draft_len ? draft_len : reinterpret_cast<const int32_t *>(out);
+    p.has_len = draft_len != nullptr;
+    p.partial = at<sv::SoftPartial>(workspace, L.partial);
+    hipError_t e = sv::launch_rejection_shard_stats(p, dtype, reinterpret_cast<sv::SoftPartial *>(out),
+                                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "shard statistics launch");
+    return SV_OK;
+}
+
+int sv_verify_rejection_partials(const sv_softmax_partial *partials, int32_t P,
+                                 const int32_t *draft, const int32_t *draft_len,
+                                 const float *uniforms, float temperature,
+                                 int32_t B, int32_t K, int32_t V,
+                                 int32_t *accepted, float *p_draft, float *q_draft,
+                                 uint32_t *flags, int64_t *stats,
+                                 sv_rejection_state *state, void *stream)
+{
+    int st;
+    if ((st = check_shard_count(P)) != SV_OK)
+        return st;
+    if (!partials || misaligned(partials, 8))
+        return fail(SV_ERR_INVALID_ARG, "partials must be non-NULL and 8-byte aligned");
+    if ((st = check_sizes(B, K, V)) != SV_OK)
+        return st;
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if (!uniforms)
+        return fail(SV_ERR_INVALID_ARG, "uniforms is NULL");
+    if ((st = check_temperature(temperature)) != SV_OK)
+        return st;
+    if (!accepted || !state || misaligned(state, 8))
+        return fail(SV_ERR_INVALID_ARG, "accepted and an 8-byte aligned state are required");
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::RejectParams p{};
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.v_full = V;
+    p.segs = P;
+    p.part_row_step = 1;
+    p.part_seg_step = static_cast<int64_t>(B) * (2 * K + 1);
+    set_temperature(p, temperature);
+    p.draft = K > 0 ? draft : accepted;
+    p.draft_len = draft_len ? draft_len : accepted;
+    p.has_len = draft_len != nullptr;
+    p.u = uniforms;
+    p.accepted = accepted;
+    p.p_draft = p_draft;
+    p.q_draft = q_draft;
+    p.flags = flags;
+    p.stats = stats;
+    p.partial = const_cast<sv::SoftPartial *>(reinterpret_cast<const sv::SoftPartial *>(partials));
+    p.seq = reinterpret_cast<sv::SeqState *>(state);
+    hipError_t e = sv::launch_rejection_decide(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "accept scan launch");
+    return SV_OK;
+}
+
+int sv_rejection_shard_mass(const void *target_logits, const void *draft_logits,
+                            int32_t dtype, int64_t row_stride,
+                            const sv_rejection_state *state, float temperature,
+                            int32_t B, int32_t K, int32_t V,
+                            sv_sample_mass *out,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if ((st = check_shard_rows(target_logits, draft_logits, dtype, row_stride, B, K, V, 0)) != SV_OK)
+        return st;
+    if ((st = check_temperature(temperature)) != SV_OK)
+        return st;
+    if (!state || misaligned(state, 8))
+        return fail(SV_ERR_INVALID_ARG, "state must be non-NULL and 8-byte aligned");
+    if (!out || misaligned(out, 8))
+        return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
+    const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
+    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype)));
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    const int nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
+    if ((st = check_grid(static_cast<int64_t>(B) * nchunks)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::RejectParams p{};
+    set_rows(p, target_logits, draft_logits, dtype, row_stride, B, K, V);
+    set_temperature(p, temperature);
+    p.seq = const_cast<sv::SeqState *>(reinterpret_cast<const sv::SeqState *>(state));
+    p.cmass = at<sv::ChunkMass>(workspace, L.cmass);
+    p.mass_out = reinterpret_cast<sv::ChunkMass *>(out);
+    hipError_t e = sv::launch_rejection_shard_mass(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "shard mass launch");
+    return SV_OK;
+}
+
+int sv_rejection_shard_sample(const void *target_logits, const void *draft_logits,
+                              int32_t dtype, int64_t row_stride,
+                              const int32_t *draft, const float *uniforms,
+                              const sv_rejection_state *state,
+                              const sv_sample_mass *masses, int32_t P, int32_t shard,
+                              float temperature, int32_t B, int32_t K, int32_t V, int32_t v_offset,
+                              int32_t *emitted,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if ((st = check_shard_rows(target_logits, draft_logits, dtype, row_stride, B, K, V, v_offset)) != SV_OK)
+        return st;
+    if ((st = check_shard_count(P)) != SV_OK)
+        return st;
+    if (shard < 0 || shard >= P)
+        return fail(SV_ERR_INVALID_ARG, "shard = %d outside [0, %d)", shard, P);
+    if (K > 0 && !draft)
+        return fail(SV_ERR_INVALID_ARG, "draft is NULL");
+    if (!uniforms)
+        return fail(SV_ERR_INVALID_ARG, "uniforms is NULL");
+    if ((st = check_temperature(temperature)) != SV_OK)
+        return st;
+    if (!state || misaligned(state, 8) || !masses || misaligned(masses, 8))
+        return fail(SV_ERR_INVALID_ARG, "state and masses must be non-NULL and 8-byte aligned");
+    if (!emitted)
+        return fail(SV_ERR_INVALID_ARG, "emitted is NULL");
+    const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
+    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype)));
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::RejectParams p{};
+    set_rows(p, target_logits, draft_logits, dtype, row_stride, B, K, V);
+    set_temperature(p, temperature);
+    p.v_offset = v_offset;
+    p.draft = K > 0 ? draft : emitted;
+    p.u = uniforms;
+    p.emitted = emitted;
+    p.seq = const_cast<sv::SeqState *>(reinterpret_cast<const sv::SeqState *>(state));
+    p.cmass = at<sv::ChunkMass>(workspace, L.cmass);
+    p.shard_mass = reinterpret_cast<const sv::ChunkMass *>(masses);
+    p.shard_count = P;
+    p.shard_index = shard;
+    hipError_t e = sv::launch_rejection_shard_sample(p, dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "shard sample launch");
     return SV_OK;
 }
 

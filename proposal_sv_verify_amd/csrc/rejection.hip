@@ -176,14 +176,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     const bool is_target = r <= K;
     const int i = is_target ? r : r - (K + 1);
     const bool needed = is_target ? i <= len : i < len;
+    // the row's draft token (target row K has none), loaded ahead of the
+    // stream and used after it when the logit at the token is captured
+    const int x = p.draft[static_cast<int64_t>(b) * K + max(0, min(i, K - 1))];
+    const int lo = seg * p.seg_len;
+    const int hi = min(p.V, lo + p.seg_len);
+    float lx = __builtin_nanf("");
 
     LaneSums ls;
     if (needed) {
         const E *rp = is_target
                           ? static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + i) * p.row_stride
                           : static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + i) * p.row_stride;
-        const int lo = seg * p.seg_len;
-        const int hi = min(p.V, lo + p.seg_len);
         const float inv_t = p.inv_t;
         const double inv_t_d = p.inv_t_d;
         const float c1 = p.split_c1, k2 = p.split_k2;
@@ -205,6 +209,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
                     careful_add<kUnitT>(f1, s, ls, inv_t, inv_t_d);
                 }
             });
+        const int xl = x - p.v_offset;
+        if (p.capture_x && i < K && xl >= lo && xl < hi)
+            lx = Elem<E>::one(rp, xl);
     }
     // the lane's sums onto its reference R, then the wave's onto their
     // largest R.  With terms summed against 0, R = max(0, rc): those terms
@@ -218,7 +225,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     const float M = wave_max(R);
     const double zz = wave_sum(R == M ? zl : rescale(zl, R, M, p.inv_t_d));
     if (lane == 0)
-        p.partial[item] = SoftPartial{zz, M, 0};
+        p.partial[item] = SoftPartial{zz, M, lx};
+}
+
+// Per-row merge of a shard's segment partials (one thread per row): the
+// segments move onto the largest reference and add up in segment order; lx
+// comes from the one segment that captured it.
+__global__ __launch_bounds__(kThreads) void k_rej_shard_rows(const RejectParams p, SoftPartial *out)
+{
+    const int64_t rows = static_cast<int64_t>(p.B) * (2 * p.K + 1);
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r >= rows)
+        return;
+    const int segs = p.segs;
+    SoftPartial q[kMaxSegs];
+#pragma unroll
+    for (int s = 0; s < kMaxSegs; ++s)
+        q[s] = p.partial[r * segs + min(s, segs - 1)];
+    float M = -__builtin_inff();
+    float lx = __builtin_nanf("");
+#pragma unroll
+    for (int s = 0; s < kMaxSegs; ++s) {
+        if (s < segs) {
+            M = fmaxf(M, q[s].m);
+            if (q[s].lx == q[s].lx)
+                lx = q[s].lx;
+        }
+    }
+    double z = 0.0;
+#pragma unroll
+    for (int s = 0; s < kMaxSegs; ++s)
+        if (s < segs)
+            z += q[s].m == M ? q[s].z : rescale(q[s].z, q[s].m, M, p.inv_t_d);
+    out[r] = SoftPartial{z, M, lx};
 }
 
 // The small kernels below issue every load of a phase before using any of
@@ -237,7 +276,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
 // draft row base + i at slot D0 + i, D0 = min(64, K + 1): for K < 64 the rows
 // are packed (2K + 1 of them).  With `publish` the workgroup also writes the
 // call's per-sequence outputs and the sequence state; every thread gets the
-// state back.
+// state back.  kShardIn: the "segments" are vocabulary shards, and the logits
+// at the draft tokens come with the partials instead of from the rows.
 constexpr int kScanRows = 128;                                 // LDS row slots, at most
 constexpr int kScanPer = kScanRows * kMaxSegs / kThreads;      // partials per thread, at most
 
@@ -245,7 +285,7 @@ __host__ __device__ constexpr int scan_rows(int K) { return (K + 1 < 64 ? K + 1 
 
 __host__ __device__ constexpr size_t scan_lds_bytes(int K, int segs)
 {
-    return static_cast<size_t>(scan_rows(K)) * (segs * 12 + 12) + sizeof(SeqState);
+    return static_cast<size_t>(scan_rows(K)) * (segs * 16 + 16) + sizeof(SeqState);
 }
 
 struct ScanLds {
@@ -253,6 +293,8 @@ struct ScanLds {
     double *Z;      // [rows]
     float *m;       // [rows * segs]
     float *M;       // [rows]
+    float *lxs;     // [rows * segs] captured logits at the draft tokens (shard input)
+    float *lx;      // [rows]
     SeqState *seq;
 
     __device__ ScanLds(char *base, int K, int segs)
@@ -263,10 +305,12 @@ struct ScanLds {
         seq = reinterpret_cast<SeqState *>(Z + rows);
         m = reinterpret_cast<float *>(seq + 1);
         M = m + static_cast<size_t>(rows) * segs;
+        lxs = M + rows;
+        lx = lxs + static_cast<size_t>(rows) * segs;
     }
 };
 
-template <typename E>
+template <typename E, bool kShardIn>
 __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool publish, const ScanLds &S,
                                            int &len_out)
 {
@@ -298,12 +342,15 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             const int rc = ci / segs;
             const int s = ci - rc * segs;
             const int ri = rc < nt ? base + rc : K + 1 + base + (rc - nt);   // row within the sequence
-            q[j] = p.partial[(row0 + ri) * segs + s];
+            q[j] = p.partial[(row0 + ri) * p.part_row_step + s * p.part_seg_step];
         }
-        const bool valid = K > 0 && x >= 0 && x < p.V;
+        const bool valid = K > 0 && x >= 0 && x < p.v_full;
         const int xc = valid ? x : 0;
-        const float lt = Elem<E>::one(static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + kc) * p.row_stride, xc);
-        const float ld = Elem<E>::one(static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + kc) * p.row_stride, xc);
+        float lt = 0.0f, ld = 0.0f;
+        if constexpr (!kShardIn) {
+            lt = Elem<E>::one(static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + kc) * p.row_stride, xc);
+            ld = Elem<E>::one(static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + kc) * p.row_stride, xc);
+        }
         const int len_raw = p.draft_len[b];
         len = p.has_len ? clamp_len(len_raw, K, fl) : K;
 #pragma unroll
@@ -318,15 +365,26 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
                 const int slot = (tgt ? rc : D0 + rc - nt) * segs + s;
                 S.m[slot] = use ? q[j].m : -__builtin_inff();
                 S.z[slot] = use ? q[j].z : 0.0;
+                if (kShardIn)
+                    S.lxs[slot] = use ? q[j].lx : __builtin_nanf("");
             }
         }
         __syncthreads();
         const int srow = t < nt ? t : (t >= D0 && t < D0 + nd ? t : -1);   // an LDS row slot, or none
         if (srow >= 0) {
             float M = -__builtin_inff();
-            for (int s = 0; s < segs; ++s)
+            float l = __builtin_nanf("");
+            for (int s = 0; s < segs; ++s) {
                 M = fmaxf(M, S.m[srow * segs + s]);
+                if (kShardIn) {
+                    const float c = S.lxs[srow * segs + s];
+                    if (c == c)
+                        l = c;
+                }
+            }
             S.M[srow] = M;
+            if (kShardIn)
+                S.lx[srow] = l;
         }
         __syncthreads();
         for (int ci = t; ci < cnt; ci += kThreads) {
@@ -352,6 +410,10 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             const bool has_t = lane < nt, has_d = lane < nd;
             const double zt = has_t ? S.Z[lane] : 0.0, zd = has_d ? S.Z[D0 + lane] : 0.0;
             const float mt = has_t ? S.M[lane] : 0.0f, md = has_d ? S.M[D0 + lane] : 0.0f;
+            if (kShardIn) {
+                lt = has_t ? S.lx[lane] : 0.0f;
+                ld = has_d ? S.lx[D0 + lane] : 0.0f;
+            }
             double pk = 0.0, qk = 0.0;
             bool rejected = false;
             if (k < len) {
@@ -380,6 +442,7 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             if (here >= 0 && k == here) {
                 SeqState sq{};
                 sq.n = here;
+                sq.len = len;
                 sq.zt = zt;
                 sq.mt = mt;
                 if (here < len) {
@@ -417,13 +480,13 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
 }
 
 // Kernel 2: one workgroup per sequence.
-template <typename E>
+template <typename E, bool kShardIn>
 __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
 {
     extern __shared__ __align__(16) char s_dyn[];
     const ScanLds S(s_dyn, p.K, p.segs);
     int len;
-    decide<E>(p, blockIdx.x, true, S, len);
+    decide<E, kShardIn>(p, blockIdx.x, true, S, len);
 }
 
 // kN consecutive elements [v0, v0 + kN) of a row, loaded before use.  kVec:
@@ -560,11 +623,28 @@ __global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
 {
     const int b = blockIdx.x / p.nchunks;
     const int c = blockIdx.x - b * p.nchunks;
-    const int len_raw = p.draft_len[b];
     const SeqState st = p.seq[b];
-    unsigned unused = 0;
-    const int len = p.has_len ? clamp_len(len_raw, p.K, unused) : p.K;
-    chunk_masses<E, kVec>(p, b, c, len, st);
+    chunk_masses<E, kVec>(p, b, c, st.len, st);
+}
+
+// A vocabulary shard's final-sample totals: the sum of its sub-chunk masses
+// per sequence, in sub-chunk order (one workgroup per sequence).
+__global__ __launch_bounds__(kThreads) void k_rej_shard_total(const RejectParams p)
+{
+    const int b = blockIdx.x;
+    const int nsub = p.nchunks * kSubPerChunk;
+    const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * nsub;
+    double r = 0.0, q = 0.0;
+    for (int k = threadIdx.x; k < nsub; k += kThreads) {
+        const ChunkMass m = cm[k];
+        r += m.r;
+        q += m.p;
+    }
+    double R, P;
+    block_inclusive_scan(r, R);
+    block_inclusive_scan(q, P);
+    if (threadIdx.x == 0)
+        p.mass_out[b] = ChunkMass{R, P};
 }
 
 // Kernel 4: one workgroup per sequence, two memory rounds.  Round 1 loads
@@ -572,10 +652,15 @@ __global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
 // state, u_K, the sequence's sub-chunk masses (kept in registers, and staged
 // in LDS when they fit) and the drafts it re-emits.  Round 2 loads the one
 // sub-chunk where the running mass crosses u_K * S.
+//
+// kShardIn (vocabulary shards): S and the mass before this shard come from
+// every shard's totals, summed in shard order; the shard where the running
+// mass crosses u_K * S (else the last one with mass) owns the sample, and
+// only its call goes on to write the sequence's emitted tokens.
 constexpr int kSelStage = 2048;                   // sub-chunk masses staged in LDS (V up to 2M)
 constexpr int kSelPer = kSelStage / kThreads;     // masses per thread held in registers
 
-template <typename E>
+template <typename E, bool kShardIn>
 __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
 {
     __shared__ ChunkMass s_cm[kSelStage];
@@ -583,8 +668,13 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
     const int K = p.K;
     const int b = blockIdx.x;
     const int t = threadIdx.x;
-    const int len_raw = p.draft_len[b];
     const SeqState st = p.seq[b];
+    ChunkMass sh[kMaxSegs];                       // every shard's totals (shard input)
+    if (kShardIn) {
+#pragma unroll
+        for (int s = 0; s < kMaxSegs; ++s)
+            sh[s] = p.shard_mass[static_cast<int64_t>(min(s, p.shard_count - 1)) * p.B + b];
+    }
     const float ufin = p.u[static_cast<int64_t>(b) * (K + 1) + K];
     const int nsub = p.nchunks * kSubPerChunk;
     const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * nsub;
@@ -617,16 +707,53 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
             myp += q.p;
         }
     }
-    unsigned unused = 0;
-    const int len = p.has_len ? clamp_len(len_raw, K, unused) : K;
+    const int len = st.len;
     const int n = st.n;
     const bool residual = n < len;
     // (the barriers inside the scans also publish s_cm)
     double SR, SP;
     const double inclr = block_inclusive_scan(myr, SR);
     const double inclp = block_inclusive_scan(myp, SP);
-    const bool use_p = !residual || SR == 0.0;
-    const double S = use_p ? SP : SR;
+    bool use_p = !residual || SR == 0.0;
+    double S = use_p ? SP : SR;
+    double base = 0.0;                            // mass before this shard
+    if (kShardIn) {
+        double tr = 0.0, tp = 0.0;
+#pragma unroll
+        for (int s = 0; s < kMaxSegs; ++s) {
+            if (s < p.shard_count) {
+                tr += sh[s].r;
+                tp += sh[s].p;
+            }
+        }
+        use_p = !residual || tr == 0.0;
+        S = use_p ? tp : tr;
+        const double u_s = static_cast<double>(ufin) * S;
+        int owner = -1, last = 0;
+        double run = 0.0, before = 0.0, before_last = 0.0;
+#pragma unroll
+        for (int s = 0; s < kMaxSegs; ++s) {
+            if (s < p.shard_count) {
+                const double X = use_p ? sh[s].p : sh[s].r;
+                if (X > 0.0) {
+                    last = s;
+                    before_last = run;
+                }
+                if (owner < 0 && run + X > u_s) {
+                    owner = s;
+                    before = run;
+                }
+                run += X;
+            }
+        }
+        if (owner < 0) {                          // rounding left u*S at or past the total
+            owner = last;
+            before = before_last;
+        }
+        if (owner != p.shard_index)
+            return;                               // uniform over the workgroup
+        base = before;
+    }
     const double thr = static_cast<double>(ufin) * S;
     int first_cs, last_c;
     auto mass = [&](int k) {
@@ -634,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
         return use_p ? q.p : q.r;
     };
     {
-        double run = use_p ? inclp - myp : inclr - myr;
+        double run = base + (use_p ? inclp - myp : inclr - myr);
         int cs = kIdxNone, lastc = -1;
         for (int k = k0; k < k1; ++k) {
             const double X = mass(k);
@@ -649,7 +776,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
     // rounding can leave u*S at or past the total: take the last sub-chunk with mass
     const int cs = first_cs != kIdxNone ? first_cs : max(last_c, 0);
     if (cs >= k0 && cs < k1) {                    // the owner knows the mass before cs
-        double run = use_p ? inclp - myp : inclr - myr;
+        double run = base + (use_p ? inclp - myp : inclr - myr);
         for (int k = k0; k < cs; ++k)             // only when a thread owns several
             run += mass(k);
         s_before = run;
@@ -683,7 +810,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
     }
     int yf, yl;
     block_first_last(first != kIdxNone, first, lastpos >= 0, lastpos, yf, yl);
-    const int y = yf != kIdxNone ? yf : yl;
+    const int y = p.v_offset + (yf != kIdxNone ? yf : yl);
     int *e = p.emitted + static_cast<int64_t>(b) * (K + 1);
     for (int k = t; k <= K; k += kThreads)
         e[k] = k < n ? (k == t ? d_own : d[k]) : (k == n ? y : -1);
@@ -704,7 +831,7 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
     if (e != hipSuccess)
         return e;
     const size_t lds = scan_lds_bytes(p.K, p.segs);
-    hipLaunchKernelGGL(k_rej_scan<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL((k_rej_scan<E, false>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
@@ -714,7 +841,45 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
         hipLaunchKernelGGL((k_rej_chunks<E, false>), g3, dim3(kThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_rej_select<E>, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((k_rej_select<E, false>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_shard_stats_typed(const RejectParams &p, SoftPartial *out, hipStream_t s)
+{
+    const int64_t rows = static_cast<int64_t>(p.B) * (2 * p.K + 1);
+    const int64_t items = rows * p.segs;
+    const dim3 g1(static_cast<unsigned>((items + kWaves - 1) / kWaves));
+    RejectParams q = p;
+    if (p.segs == 1)
+        q.partial = out;                          // one segment per row: already merged
+    if (sizeof(E) == 2 && p.split_ok)
+        hipLaunchKernelGGL((k_rej_stats<E, kExpSplit>), g1, dim3(kThreads), 0, s, q);
+    else if (p.inv_t == 1.0f)
+        hipLaunchKernelGGL((k_rej_stats<E, kExpUnitT>), g1, dim3(kThreads), 0, s, q);
+    else
+        hipLaunchKernelGGL((k_rej_stats<E, kExpScaled>), g1, dim3(kThreads), 0, s, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.segs == 1)
+        return e;
+    hipLaunchKernelGGL(k_rej_shard_rows, dim3(static_cast<unsigned>((rows + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, p, out);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_shard_mass_typed(const RejectParams &p, hipStream_t s)
+{
+    const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
+    if (p.vec_ok)
+        hipLaunchKernelGGL((k_rej_chunks<E, true>), g3, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_rej_chunks<E, false>), g3, dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_rej_shard_total, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -723,6 +888,33 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
 hipError_t launch_rejection(const RejectParams &p, int dtype, hipStream_t s)
 {
     return dtype == SV_BF16 ? launch_typed<uint16_t>(p, s) : launch_typed<float>(p, s);
+}
+
+hipError_t launch_rejection_shard_stats(const RejectParams &p, int dtype, SoftPartial *out, hipStream_t s)
+{
+    return dtype == SV_BF16 ? launch_shard_stats_typed<uint16_t>(p, out, s)
+                            : launch_shard_stats_typed<float>(p, out, s);
+}
+
+hipError_t launch_rejection_decide(const RejectParams &p, hipStream_t s)
+{
+    const size_t lds = scan_lds_bytes(p.K, p.segs);
+    hipLaunchKernelGGL((k_rej_scan<float, true>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_rejection_shard_mass(const RejectParams &p, int dtype, hipStream_t s)
+{
+    return dtype == SV_BF16 ? launch_shard_mass_typed<uint16_t>(p, s) : launch_shard_mass_typed<float>(p, s);
+}
+
+hipError_t launch_rejection_shard_sample(const RejectParams &p, int dtype, hipStream_t s)
+{
+    if (dtype == SV_BF16)
+        hipLaunchKernelGGL((k_rej_select<uint16_t, true>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_rej_select<float, true>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
 }
 
 } // namespace sv

@@ -25,11 +25,14 @@ struct ArgPartial {
 };
 
 // Per-(row, segment) softmax partial: z = sum exp((l - m) / T) over the
-// segment, m = the segment's largest raw logit.
+// segment against the reference m (at least the segment's largest logit's
+// neighbourhood; see the statistics kernel).  lx: the logit at the row's
+// draft token when a vocabulary-shard call captures it and the token lies in
+// the segment, else NaN.  Same layout as the public sv_softmax_partial.
 struct SoftPartial {
     double z;
     float m;
-    int pad;
+    float lx;
 };
 
 // Per-chunk masses of the final sample.
@@ -38,12 +41,13 @@ struct ChunkMass {
     double p;   // sum of p over the chunk
 };
 
-// Per-sequence state handed from the chunk kernel to the selection kernel.
+// Per-sequence state handed from the accept scan to the final-sample
+// kernels (same layout as the public sv_rejection_state).
 struct SeqState {
     double zt, zd;   // normalisers of target row n and draft row n
-    float mt, md;    // raw maxima of those rows
+    float mt, md;    // their references
     int n;           // accepted drafts
-    int pad;
+    int len;         // the sequence's draft length (n < len: residual sample)
 };
 
 // Greedy and tree verification: a streaming argmax per (row, segment), then
@@ -106,6 +110,19 @@ struct RejectParams {
     float split_c1;
     float split_k2;
     int32_t split_ok;
+    // vocabulary shards: V above is the shard's width and the logit pointers
+    // address its columns; v_offset is its first global id.  capture_x: the
+    // statistics kernel records each row's logit at its draft token.
+    int32_t v_offset;
+    int32_t capture_x;
+    // accept scan: segment s of row r at partial[r * part_row_step + s *
+    // part_seg_step]; v_full bounds valid draft ids (the full vocabulary)
+    int64_t part_row_step, part_seg_step;
+    int32_t v_full;
+    // owner-shard sampling: masses[s * B + b] of shard s, shard_index = this one
+    const ChunkMass *shard_mass;
+    int32_t shard_count, shard_index;
+    ChunkMass *mass_out;      // [B] the shard's totals
     // draft, draftl and draft_len always point at valid memory, so kernels can
     // load from them unconditionally: with K == 0 draft and draftl stand in
     // for nothing (any int array, the target logits), and without lengths
@@ -127,6 +144,13 @@ struct RejectParams {
 };
 
 hipError_t launch_rejection(const RejectParams &p, int dtype, hipStream_t s);
+// vocabulary-shard pieces: statistics (then a per-row merge when rows are
+// cut into segments), the accept scan on per-shard partials, the shard's
+// final-sample masses, and the owner shard's sample
+hipError_t launch_rejection_shard_stats(const RejectParams &p, int dtype, SoftPartial *out, hipStream_t s);
+hipError_t launch_rejection_decide(const RejectParams &p, hipStream_t s);
+hipError_t launch_rejection_shard_mass(const RejectParams &p, int dtype, hipStream_t s);
+hipError_t launch_rejection_shard_sample(const RejectParams &p, int dtype, hipStream_t s);
 
 struct NgramParams {
     const int32_t *tokens;

@@ -198,3 +198,73 @@ def test_shard_calls_reject_bad_arguments(lib):
     assert tree(path=None) == sv.SV_ERR_INVALID_ARG
     for f in (shard, greedy, tree):
         assert lib.sv_last_error_message()
+
+
+def test_rejection_shard_calls_reject_bad_arguments(lib):
+    F = 1.0
+
+    def stats(**kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, rs=128, draft=FAKE, dl=None, T=F, B=2, K=3, V=100,
+                 off=0, out=FAKE, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_rejection_shard_stats(a["t"], a["d"], a["dtype"], a["rs"], a["draft"],
+                                            a["dl"], a["T"], a["B"], a["K"], a["V"], a["off"],
+                                            a["out"], a["ws"], a["wsb"], None)
+    assert stats(B=0) == sv.SV_ERR_INVALID_ARG
+    assert stats(off=-1) == sv.SV_ERR_INVALID_ARG
+    assert stats(off=(1 << 30) - 50) == sv.SV_ERR_UNSUPPORTED
+    assert stats(rs=99) == sv.SV_ERR_INVALID_ARG
+    assert stats(draft=None) == sv.SV_ERR_INVALID_ARG
+    assert stats(T=0.0) == sv.SV_ERR_INVALID_ARG
+    assert stats(T=float("inf")) == sv.SV_ERR_INVALID_ARG
+    assert stats(out=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert stats(wsb=8) == sv.SV_ERR_WORKSPACE
+    assert lib.sv_rejection_shard_workspace_bytes(0, 3, 100) == 0
+    assert lib.sv_rejection_shard_workspace_bytes(64, 5, 16032) > 0
+
+    def decide(**kw):
+        a = dict(parts=FAKE, P=4, draft=FAKE, dl=None, u=FAKE, T=F, B=2, K=3, V=100, acc=FAKE,
+                 state=FAKE)
+        a.update(kw)
+        return lib.sv_verify_rejection_partials(a["parts"], a["P"], a["draft"], a["dl"], a["u"],
+                                                a["T"], a["B"], a["K"], a["V"], a["acc"], None,
+                                                None, None, None, a["state"], None)
+    assert decide(P=0) == sv.SV_ERR_INVALID_ARG
+    assert decide(P=sv.MAX_REJECT_SHARDS + 1) == sv.SV_ERR_UNSUPPORTED
+    assert decide(parts=None) == sv.SV_ERR_INVALID_ARG
+    assert decide(parts=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert decide(u=None) == sv.SV_ERR_INVALID_ARG
+    assert decide(T=-1.0) == sv.SV_ERR_INVALID_ARG
+    assert decide(state=None) == sv.SV_ERR_INVALID_ARG
+    assert decide(state=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert decide(acc=None) == sv.SV_ERR_INVALID_ARG
+
+    def mass(**kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, rs=128, state=FAKE, T=F, B=2, K=3, V=100, out=FAKE,
+                 ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_rejection_shard_mass(a["t"], a["d"], a["dtype"], a["rs"], a["state"], a["T"],
+                                           a["B"], a["K"], a["V"], a["out"], a["ws"], a["wsb"],
+                                           None)
+    assert mass(state=None) == sv.SV_ERR_INVALID_ARG
+    assert mass(out=None) == sv.SV_ERR_INVALID_ARG
+    assert mass(K=-1) == sv.SV_ERR_INVALID_ARG
+    assert mass(wsb=8) == sv.SV_ERR_WORKSPACE
+
+    def sample(**kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, rs=128, draft=FAKE, u=FAKE, state=FAKE, masses=FAKE,
+                 P=3, shard=1, T=F, B=2, K=3, V=100, off=0, emi=FAKE, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_rejection_shard_sample(a["t"], a["d"], a["dtype"], a["rs"], a["draft"],
+                                             a["u"], a["state"], a["masses"], a["P"], a["shard"],
+                                             a["T"], a["B"], a["K"], a["V"], a["off"], a["emi"],
+                                             a["ws"], a["wsb"], None)
+    assert sample(shard=3) == sv.SV_ERR_INVALID_ARG
+    assert sample(shard=-1) == sv.SV_ERR_INVALID_ARG
+    assert sample(P=17) == sv.SV_ERR_UNSUPPORTED
+    assert sample(masses=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert sample(emi=None) == sv.SV_ERR_INVALID_ARG
+    assert sample(u=None) == sv.SV_ERR_INVALID_ARG
+    assert sample(wsb=8) == sv.SV_ERR_WORKSPACE
+    for f in (stats, decide, mass, sample):
+        assert lib.sv_last_error_message()

@@ -13,7 +13,7 @@ import torch
 
 import proposal_sv_verify_amd as sv
 from proposal_sv_verify_amd import workloads as W
-from gpu_util import dev, host, say, to_dev
+from gpu_util import check_rejection, dev, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +122,119 @@ def test_greedy_partials_full_size_eight_shards():
         ref = sv.verify_greedy(lt, dr)
         for k in ("accepted", "emitted", "argmax"):
             np.testing.assert_array_equal(host(got[k]), host(ref[k]), err_msg="%s alpha %.1f" % (k, a))
+
+
+# ------------------------------------------------------------ rejection sampling
+#
+# Sharded rejection sampling takes four steps per call: per-shard row
+# statistics, the accept test on all shards' partials, per-shard sample
+# masses, and the owner shard's sample.  Its decisions must match the oracle
+# (and the unsharded call) except within the rounding band of a tie, which
+# the oracle flags.
+
+def _rejection_sharded(wl, shards, draft_len=None):
+    B, K, V, T = wl["B"], wl["K"], wl["V"], wl["temperature"]
+    tg, dg = to_dev(wl["target"]), to_dev(wl["draft_logits"])
+    dr, u = to_dev(wl["draft"]), to_dev(wl["uniforms"])
+    dl = to_dev(draft_len) if draft_len is not None else None
+    P = len(shards)
+    parts = torch.empty(P, B * (2 * K + 1), 2, dtype=torch.float64, device=dev())
+    for p, (a, b) in enumerate(shards):
+        sv.rejection_shard_stats(tg[..., a:b], dg[..., a:b], dr, a, T, dl, out=parts[p])
+    stats = torch.zeros(3 + K, dtype=torch.int64, device=dev())
+    dec = sv.verify_rejection_partials(parts, dr, u, V, T, dl, stats=stats)
+    masses = torch.empty(P, B, 2, dtype=torch.float64, device=dev())
+    wss = []
+    for p, (a, b) in enumerate(shards):
+        m = sv.rejection_shard_mass(tg[..., a:b], dg[..., a:b], dec["state"], T, out=masses[p])
+        wss.append(m["workspace"])
+    emitted = torch.full((B, K + 1), -7, dtype=torch.int32, device=dev())
+    for p, (a, b) in enumerate(shards):
+        sv.rejection_shard_sample(tg[..., a:b], dg[..., a:b], dr, u, dec["state"], masses, p, a,
+                                  wss[p], emitted, T)
+    out = dict(dec)
+    out["emitted"] = emitted
+    out["stats"] = stats
+    out["parts"] = parts
+    return out
+
+
+def _check_soft_partials(parts, wl, shards, draft_len=None):
+    """Each shard's per-row (z, m) gives the shard's log-sum-exp of l / T,
+    and lx is the logit at the row's draft token when the shard holds it."""
+    B, K, T = wl["B"], wl["K"], wl["temperature"]
+    got = host(parts).view(sv.SOFT_PARTIAL_DTYPE).reshape(len(shards), B, 2 * K + 1)
+    wide = lambda a: (W.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+    tg, dg = wide(wl["target"]), wide(wl["draft_logits"])
+    lens = np.full(B, K) if draft_len is None else np.clip(draft_len, 0, K)
+    for p, (a, b) in enumerate(shards):
+        for bb in range(B):
+            for r in range(2 * K + 1):
+                is_t = r <= K
+                i = r if is_t else r - K - 1
+                g = got[p, bb, r]
+                if not (i <= lens[bb] if is_t else i < lens[bb]):
+                    assert g["z"] == 0.0 and g["m"] == -np.inf
+                    continue
+                row = (tg[bb, i] if is_t else dg[bb, i])[a:b] / T
+                lse = np.logaddexp.reduce(row)
+                mine = np.log(g["z"]) + np.float64(g["m"]) / T
+                np.testing.assert_allclose(mine, lse, rtol=0, atol=1e-6 * max(1.0, abs(lse)))
+                x = wl["draft"][bb, i] if i < K else -1
+                if i < K and a <= x < b:
+                    src = (tg[bb, i] if is_t else dg[bb, i])
+                    assert np.float64(g["lx"]) == src[x]
+                else:
+                    assert np.isnan(g["lx"])
+
+
+def _rejection_shard_case(orc, wl, shards, draft_len=None, label=""):
+    say("sharded rejection", label, "P", len(shards), shards[:4])
+    g = _rejection_sharded(wl, shards, draft_len)
+    r = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], wl["uniforms"],
+                             wl["temperature"], draft_len)
+    flagged, mism = check_rejection(g, r, label)
+    np.testing.assert_array_equal(host(g["flags"]).astype(np.uint32), r["flags"])
+    acc = host(g["accepted"]).astype(np.int64)
+    assert host(g["stats"])[0] == acc.sum() and host(g["stats"])[2] == (acc + 1).sum()
+    # the unsharded call on the same inputs: the same except at flagged ties
+    u = sv.verify_rejection(to_dev(wl["target"]), to_dev(wl["draft_logits"]), to_dev(wl["draft"]),
+                            to_dev(wl["uniforms"]), wl["temperature"],
+                            to_dev(draft_len) if draft_len is not None else None)
+    tie = r["accept_tie"] | r["sample_tie"]
+    same = (host(u["emitted"]) == host(g["emitted"])).all(axis=1)
+    assert (same | tie).all(), "%s: sharded and unsharded differ outside flagged ties" % label
+    return g, flagged, mism
+
+
+@pytest.mark.parametrize("dtype,T,P,ragged", [("bf16", 1.0, 3, False), ("f32", 0.7, 5, True),
+                                              ("bf16", 1.3, 2, True), ("f32", 1.0, 16, False)])
+def test_rejection_sharded_matches_oracle(orc, dtype, T, P, ragged):
+    B, K, V = 12, 5, 30000
+    wl = W.rejection_workload(B, K, V, 2.0, 0.5, T, seed=700 + P, dtype=dtype)
+    rng = np.random.default_rng(80 + P)
+    shards = _cuts(V, P, rng)
+    dl = rng.integers(-1, K + 2, size=B).astype(np.int32) if ragged else None
+    g, _, _ = _rejection_shard_case(orc, wl, shards, dl, "%s T%.1f P%d" % (dtype, T, P))
+    _check_soft_partials(g["parts"], wl, shards, dl)
+
+
+def test_rejection_sharded_bonus_only_and_masked(orc):
+    """K = 0 (every call samples the bonus from p) and top-k masked rows,
+    where whole shards of a row are -inf."""
+    wl = W.rejection_workload(9, 0, 7000, 2.0, 0.5, 1.0, seed=733, dtype="bf16")
+    _rejection_shard_case(orc, wl, _cuts(7000, 4, np.random.default_rng(3)), label="K0 P4")
+    wl = W.rejection_workload(16, 4, 40000, 2.0, 0.7, 1.0, seed=734, dtype="bf16", top_k=40)
+    _rejection_shard_case(orc, wl, [(i * 5000, (i + 1) * 5000) for i in range(8)],
+                          label="top40 P8")
+
+
+def test_rejection_sharded_full_size_eight_shards(orc):
+    """B 64, K 5, V 128256 bf16 in the eight 16032-column shards of an
+    8-way tensor-parallel output layer."""
+    wl = W.rejection_workload(**W.REJECTION, seed=W.seed_for(3))
+    V = wl["V"]
+    shards = [(i * V // 8, (i + 1) * V // 8) for i in range(8)]
+    _, flagged, mism = _rejection_shard_case(orc, wl, shards, label="full size P8")
+    say("sharded rejection full size: flagged %d, mismatched %d of 64" % (flagged, mism))
+    assert mism <= flagged
