@@ -33,6 +33,10 @@ FLAG_BAD_PARENT = 4
 # relative errors of at most one fp32 ulp (2^-23) has a CDF error with
 # standard deviation at most 2 * 2^-23 * sqrt(sum p^2 + sum q^2), so the band
 # is eight standard deviations wide.
+# Suffix decoding counts the continuations of at most this many of the
+# matched pattern's most recent occurrences in each text.
+SUFFIX_OCC_CAP = 256
+
 ACCEPT_BAND = 1e-6
 SAMPLE_BAND_SCALE = 16.0 * 2.0 ** -23
 
@@ -93,6 +97,9 @@ class Oracle:
         L.orc_verify_tree.restype = None
         L.orc_ngram_propose.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P, P]
         L.orc_ngram_propose.restype = None
+        L.orc_suffix_propose.argtypes = [P, i64, P, i32, P, i64, i32, i32, i32, dbl, i32, P, P, P,
+                                         P, P, P]
+        L.orc_suffix_propose.restype = None
         self.lib = L
         self.path = path
 
@@ -175,6 +182,29 @@ class Oracle:
         return dict(proposal=prop, proposal_len=plen, match_n=mn, match_pos=mp, flags=flg)
 
 
+    def suffix_propose(self, tokens, lengths, history, m_min, m_max, K, min_prob,
+                       occ_cap=SUFFIX_OCC_CAP):
+        """tokens [B, stride] int32, lengths [B] int32, history [H] int32
+        (None or empty for none)."""
+        tokens = _i32(tokens)
+        B, stride = tokens.shape
+        lengths = _i32(lengths).reshape(B)
+        hist = None if history is None else _i32(history).reshape(-1)
+        H = 0 if hist is None else hist.size
+        prop = np.zeros((B, K), np.int32)
+        plen = np.zeros(B, np.int32)
+        sco = np.zeros(B, np.float64)
+        ml = np.zeros(B, np.int32)
+        src = np.zeros(B, np.int32)
+        flg = np.zeros(B, np.uint32)
+        self.lib.orc_suffix_propose(_ptr(tokens), stride, _ptr(lengths), B,
+                                    _ptr(hist) if H > 0 else None, H, m_min, m_max, K,
+                                    float(min_prob), occ_cap, _ptr(prop), _ptr(plen), _ptr(sco),
+                                    _ptr(ml), _ptr(src), _ptr(flg))
+        return dict(proposal=prop, proposal_len=plen, score=sco, match_len=ml, source=src,
+                    flags=flg)
+
+
 _default = None
 
 
@@ -206,6 +236,10 @@ def verify_tree(*a, **k):
 
 def ngram_propose(*a, **k):
     return default().ngram_propose(*a, **k)
+
+
+def suffix_propose(*a, **k):
+    return default().suffix_propose(*a, **k)
 
 
 # ---------------------------------------------------------------- adaptive length

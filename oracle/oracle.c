@@ -392,3 +392,159 @@ void orc_ngram_propose(const int32_t *tokens, int64_t ctx_stride,
             flags[b] = fl;
     }
 }
+
+/* ------------------------------------------------------------------ suffix
+ * [Arctic] "suffix decoding": suffix trees over the current prompt and over
+ * earlier outputs are searched with the most recently generated tokens, and
+ * each candidate token is ranked by its frequency (an empirical
+ * probability); the candidate sequence is as long as it stays likely.  A
+ * suffix tree answers "where does this pattern occur, and what followed
+ * it"; the oracle answers the same questions directly from the texts.
+ */
+
+/* Length of the common suffix of text[..e] and the context c[..L-1], at
+ * most m_max; a context token below 0 never matches. */
+static int32_t suffix_match(const int32_t *text, int64_t e, const int32_t *c, int64_t L,
+                            int32_t m_max)
+{
+    int32_t m = 0;
+    while (m < m_max && e - m >= 0 && L - 1 - m >= 0 && c[L - 1 - m] >= 0 &&
+           text[e - m] == c[L - 1 - m])
+        ++m;
+    return m;
+}
+
+/* One text.  An occurrence is an end position e whose next token exists and
+ * is a token (text[e + 1] >= 0).  The pattern is the longest context suffix
+ * (m_min <= length <= m_max) with an occurrence; the occ_cap most recent
+ * occurrences are counted.  Depth by depth, the next candidate is the token
+ * that follows the current path most often among them (lowest id on equal
+ * counts); its probability is that count over the number of occurrences,
+ * and the path stops before a token whose probability is below min_prob, or
+ * when nothing follows.  Returns the path length; *n_occ, *count_sum (the
+ * sum of the counts) and *m_star describe the match. */
+static int32_t suffix_one(const int32_t *text, int64_t len_t, const int32_t *c, int64_t L,
+                          int32_t m_min, int32_t m_max, int32_t K, double min_prob,
+                          int32_t occ_cap, int64_t *occ, unsigned char *alive,
+                          int32_t *path, int32_t *n_occ, int64_t *count_sum, int32_t *m_star)
+{
+    int32_t best = 0;
+    for (int64_t e = len_t - 2; e >= 0; --e) {
+        if (text[e + 1] < 0)
+            continue;
+        const int32_t m = suffix_match(text, e, c, L, m_max);
+        if (m > best)
+            best = m;
+    }
+    *n_occ = 0;
+    *count_sum = 0;
+    *m_star = 0;
+    if (best < m_min || best == 0)
+        return 0;
+    int32_t n = 0;
+    for (int64_t e = len_t - 2; e >= 0 && n < occ_cap; --e)
+        if (text[e + 1] >= 0 && suffix_match(text, e, c, L, m_max) == best)
+            occ[n++] = e;
+    for (int32_t i = 0; i < n; ++i)
+        alive[i] = 1;
+    int32_t len = 0;
+    int64_t sum = 0;
+    for (int32_t j = 1; j <= K; ++j) {
+        int32_t tok = -1;
+        int64_t cnt_best = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            if (!alive[i] || occ[i] + j >= len_t || text[occ[i] + j] < 0)
+                continue;
+            const int32_t t = text[occ[i] + j];
+            int64_t cnt = 0;
+            for (int32_t k = 0; k < n; ++k)
+                if (alive[k] && occ[k] + j < len_t && text[occ[k] + j] == t)
+                    ++cnt;
+            if (cnt > cnt_best || (cnt == cnt_best && t < tok)) {
+                cnt_best = cnt;
+                tok = t;
+            }
+        }
+        if (cnt_best == 0 || (double)cnt_best < min_prob * (double)n)
+            break;
+        path[len++] = tok;
+        sum += cnt_best;
+        for (int32_t i = 0; i < n; ++i)
+            alive[i] = alive[i] && occ[i] + j < len_t && text[occ[i] + j] == tok;
+    }
+    *n_occ = n;
+    *count_sum = sum;
+    *m_star = best;
+    return len;
+}
+
+void orc_suffix_propose(const int32_t *tokens, int64_t ctx_stride,
+                        const int32_t *lengths, int32_t B,
+                        const int32_t *history, int64_t H,
+                        int32_t m_min, int32_t m_max, int32_t K, double min_prob,
+                        int32_t occ_cap,
+                        int32_t *proposal, int32_t *proposal_len, double *score,
+                        int32_t *match_len, int32_t *source, uint32_t *flags)
+{
+    int64_t *occ = (int64_t *)malloc(sizeof(int64_t) * (size_t)(occ_cap > 0 ? occ_cap : 1));
+    unsigned char *alive = (unsigned char *)malloc((size_t)(occ_cap > 0 ? occ_cap : 1));
+    int32_t *path_c = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    int32_t *path_h = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1));
+    for (int32_t b = 0; b < B; ++b) {
+        uint32_t fl = 0;
+        const int32_t *c = tokens + (size_t)b * (size_t)ctx_stride;
+        int64_t L = lengths[b];
+        if (L < 0 || L > ctx_stride) {
+            fl |= ORC_FLAG_BAD_LEN;
+            L = 0;
+        }
+        int32_t nc, nh, mc, mh;
+        int64_t sc, sh;
+        const int32_t lc = suffix_one(c, L, c, L, m_min, m_max, K, min_prob, occ_cap, occ, alive,
+                                      path_c, &nc, &sc, &mc);
+        int32_t lh = 0;
+        nh = 0;
+        sh = 0;
+        mh = 0;
+        if (history && H > 0)
+            lh = suffix_one(history, H, c, L, m_min, m_max, K, min_prob, occ_cap, occ, alive,
+                            path_h, &nh, &sh, &mh);
+        /* the higher expected number of accepted tokens, sc/nc against
+         * sh/nh (exact in integers); the context wins ties */
+        int which = -1;
+        if (lc > 0 && (lh == 0 || sc * (int64_t)nh >= sh * (int64_t)nc))
+            which = 0;
+        else if (lh > 0)
+            which = 1;
+        int32_t *pr = proposal + (size_t)b * K;
+        for (int32_t k = 0; k < K; ++k)
+            pr[k] = -1;
+        int32_t len = 0;
+        double sco = 0.0;
+        int32_t ml = 0;
+        if (which == 0) {
+            len = lc;
+            for (int32_t k = 0; k < lc; ++k)
+                pr[k] = path_c[k];
+            sco = (double)sc / (double)nc;
+            ml = mc;
+        } else if (which == 1) {
+            len = lh;
+            for (int32_t k = 0; k < lh; ++k)
+                pr[k] = path_h[k];
+            sco = (double)sh / (double)nh;
+            ml = mh;
+        }
+        proposal_len[b] = len;
+        score[b] = sco;
+        match_len[b] = ml;
+        if (source)
+            source[b] = which;
+        if (flags)
+            flags[b] = fl;
+    }
+    free(occ);
+    free(alive);
+    free(path_c);
+    free(path_h);
+}

@@ -123,6 +123,27 @@ void orc_ngram_propose(const int32_t *tokens, int64_t ctx_stride,
                        int32_t *proposal, int32_t *proposal_len,
                        int32_t *match_n, int32_t *match_pos, uint32_t *flags);
 
+/*
+ * Suffix-decoding proposal ([Arctic] "suffix decoding": the recent tokens
+ * are matched against suffix trees of the current prompt and of earlier
+ * outputs, and candidate tokens are ranked by how often they followed).
+ * tokens [B][ctx_stride] with lengths [B] (the current contexts);
+ * history [H] (earlier outputs, one shared text; negative entries separate
+ * documents and never match or continue); occ_cap = how many of the most
+ * recent occurrences of the matched pattern are counted.
+ * Outputs: proposal [B][K] (-1 padded), proposal_len [B], score [B] (the
+ * expected number of accepted tokens, sum of the path's probabilities),
+ * match_len [B] (the matched pattern's length, 0 when none), source [B]
+ * (0 context, 1 history, -1 none) or NULL, flags [B] or NULL.
+ */
+void orc_suffix_propose(const int32_t *tokens, int64_t ctx_stride,
+                        const int32_t *lengths, int32_t B,
+                        const int32_t *history, int64_t H,
+                        int32_t m_min, int32_t m_max, int32_t K, double min_prob,
+                        int32_t occ_cap,
+                        int32_t *proposal, int32_t *proposal_len, double *score,
+                        int32_t *match_len, int32_t *source, uint32_t *flags);
+
 #ifdef __cplusplus
 }
 #endif

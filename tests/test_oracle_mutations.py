@@ -14,6 +14,7 @@ import pytest
 import oracle
 import test_oracle_greedy as G
 import test_oracle_rejection as R
+import test_oracle_suffix as SX
 import test_oracle_tree_ngram as TN
 from conftest import golden
 
@@ -34,6 +35,11 @@ TREE_PINS = [TN.test_tree_single_node, TN.test_tree_equal_depth_tie_lowest_id,
              TN.test_random_trees_brute_force]
 NGRAM_PINS = [TN.test_ngram_overlap_short_and_ragged, TN.test_ngram_planted_copy,
               TN.test_ngram_exhaustive_ternary]
+SUFFIX_PINS = [SX.test_worked_example, SX.test_history_tree_and_separators,
+               SX.test_better_text_wins_and_context_wins_ties,
+               SX.test_periodic_context_continues_the_period,
+               SX.test_one_occurrence_reduces_to_ngram_lookup,
+               lambda o: SX.test_exhaustive_ternary_against_brute_force(o, 1, 3, 3, 0.0, 256)]
 
 MUTANTS = [
     ("argmax keeps the last maximum", "if (x > bv) {", "if (x >= bv) {", GREEDY_PINS),
@@ -67,6 +73,22 @@ MUTANTS = [
      "pr[k] = c[got_s + k];", NGRAM_PINS),
     ("n-gram lets the suffix match itself", "for (int64_t s = L - n - 1; s >= 0; --s) {",
      "for (int64_t s = L - n; s >= 0; --s) {", NGRAM_PINS),
+    ("suffix counts the oldest occurrences",
+     "for (int64_t e = len_t - 2; e >= 0 && n < occ_cap; --e)",
+     "for (int64_t e = 0; e <= len_t - 2 && n < occ_cap; ++e)", SUFFIX_PINS),
+    ("suffix ties go to the larger id", "(cnt == cnt_best && t < tok)",
+     "(cnt == cnt_best && t > tok)", SUFFIX_PINS),
+    ("suffix path does not narrow the occurrences",
+     "alive[i] = alive[i] && occ[i] + j < len_t && text[occ[i] + j] == tok;",
+     "alive[i] = alive[i] && occ[i] + j < len_t;", SUFFIX_PINS),
+    ("suffix ignores document separators", "        if (text[e + 1] < 0)\n            continue;",
+     "", SUFFIX_PINS),
+    ("suffix prefers the history on equal scores", "sc * (int64_t)nh >= sh * (int64_t)nc",
+     "sc * (int64_t)nh > sh * (int64_t)nc", SUFFIX_PINS),
+    ("suffix score counts tokens, not probabilities", "sum += cnt_best;", "sum += n;",
+     SUFFIX_PINS),
+    ("suffix takes the shortest pattern", "if (m > best)", "if (m > 0 && (best == 0 || m < best))",
+     SUFFIX_PINS),
 ]
 
 
