@@ -173,6 +173,33 @@ def _timed(fns, reps):
     return ev[0].elapsed_time(ev[1]) * 1e3 / reps
 
 
+def suffix_proposer(reps=30):
+    """Suffix-decoding proposals for the 64 n-gram contexts (8192 tokens)
+    against a shared 262144-token history: HIP-event mean per call.  The
+    texts hold 4 * (64 * 8192 + 262144) bytes; each sequence scans the
+    history itself (64 reads of it, mostly from cache)."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    from proposal_sv_verify_amd import workloads as W
+
+    c = W.SUFFIX
+    wl = W.suffix_workload(c["B"], c["L"], c["H"], seed=W.seed_for(2, salt=7))
+    dev = torch.device("cuda:0")
+    tok = torch.from_numpy(wl["tokens"]).to(dev)
+    lens = torch.from_numpy(wl["lengths"]).to(dev)
+    hist = torch.from_numpy(wl["history"]).to(dev)
+    call = sv.prepare_suffix(tok, lens, hist, c["m_min"], c["m_max"], c["K"], c["min_prob"])
+    us = _timed([call], reps)
+    out = {k: v.cpu().numpy() for k, v in call().items()}
+    text_bytes = 4 * (c["B"] * c["L"] + c["H"])
+    return dict(contexts=c["B"], context_len=c["L"], history=c["H"], m_max=c["m_max"], K=c["K"],
+                min_prob=c["min_prob"], us_per_call=round(us, 2),
+                proposals_per_s=round(c["B"] / us * 1e6, 1), text_bytes=text_bytes,
+                gb_per_s_text=round(text_bytes / us / 1e3, 1),
+                mean_proposal_len=round(float(out["proposal_len"].mean()), 3),
+                from_history=int((out["source"] == 1).sum()))
+
+
 def rejection_shards(d, shards=8, reps=30):
     """The rejection workload in the eight 16032-column vocabulary shards
     of an 8-way tensor-parallel output layer: per-shard statistics, the
@@ -347,6 +374,8 @@ def main():
                     help="skip the 16384-context n-gram measurement")
     ap.add_argument("--no-shards", action="store_true",
                     help="skip the vocabulary-sharded greedy and rejection measurements")
+    ap.add_argument("--no-suffix", action="store_true",
+                    help="skip the suffix-decoding proposer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy a 256 MiB device buffer three times (a "
                          "kernel of known traffic for scaling the rocprofv3 byte counters)")
@@ -402,6 +431,8 @@ def main():
                   roofline=roofline, kernels=kernels)
     if not args.no_bandwidth_mode:
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
+    if not args.no_suffix:
+        result["suffix_proposer"] = suffix_proposer()
     if not args.no_shards:
         result["greedy_vocab_shards"] = greedy_shards(gr)
         result["rejection_vocab_shards"] = rejection_shards(dev_inputs)

@@ -89,6 +89,9 @@ extern "C" {
 #define SV_MAX_TREE_NODES 1024      /* N of sv_verify_tree */
 #define SV_MAX_NGRAM 31             /* n_max of sv_ngram_propose */
 #define SV_MAX_CONTEXT (1 << 26)    /* n-gram context length / ctx_stride */
+#define SV_SUFFIX_MAX_MATCH 32      /* m_max of sv_suffix_propose */
+#define SV_SUFFIX_MAX_K 32          /* K of sv_suffix_propose */
+#define SV_SUFFIX_OCC 256           /* occurrences counted per text */
 #define SV_MAX_PROPOSAL 4096        /* K of sv_ngram_propose */
 #define SV_MAX_DRAFTS 4096          /* K of the verifiers */
 
@@ -377,6 +380,46 @@ typedef struct {
 int sv_adaptive_init(sv_adaptive *state, const int32_t *tiers, int32_t ntiers, double beta,
                      double ema0);
 int sv_adaptive_update(sv_adaptive *state, double accepted_mean);
+
+/*
+ * sv_suffix_propose -- [Arctic] "suffix decoding": the most recent tokens
+ * are looked up in suffix trees of the current prompt and of earlier
+ * outputs, candidate tokens are ranked by how often they followed (an
+ * empirical probability), and the candidate sequence grows while it stays
+ * likely.  Per sequence b, for each text T (its context c = tokens[b][0..L),
+ * L = lengths[b]; and the shared history[0..H)):
+ *   an occurrence is an end position e with a token after it (T[e+1] >= 0;
+ *   negative entries separate history documents and never match);
+ *   m(e) = the common suffix length of T[..e] and c, at most m_max;
+ *   the pattern length m* = the largest m(e) (a text with m* < m_min has
+ *   no candidates); the SV_SUFFIX_OCC most recent occurrences with
+ *   m(e) = m* (n of them) are counted;
+ *   step j = 1..K: among the occurrences that continue with the path so
+ *   far, the most frequent next token x_j (lowest id on equal counts),
+ *   count_j of them; the path stops before a step with count_j <
+ *   min_prob * n (in fp64) or with nothing following;
+ *   score = sum of count_j / n (the expected number of accepted tokens).
+ * The text with the larger score gives the proposal (the context on equal
+ * scores; compared exactly); no text with a path: proposal_len 0.
+ *
+ *   tokens [B][ctx_stride] int32, lengths [B] int32 (outside
+ *   [0, ctx_stride]: flagged SV_FLAG_BAD_LEN, treated as 0)
+ *   history [H] int32 or NULL (H = 0)
+ *   proposal [B][K] (-1 padded), proposal_len [B] (out)
+ *   score [B] double, match_len [B] (m* of the chosen text, 0 if none),
+ *   source [B] (0 context, 1 history, -1 none), flags [B]: each NULL or out
+ *   workspace as sized by sv_suffix_workspace_bytes(B, ctx_stride, H).
+ * Limits: 1 <= B, 1 <= m_min <= m_max <= SV_SUFFIX_MAX_MATCH,
+ *         0 <= K <= SV_SUFFIX_MAX_K, 0 <= min_prob <= 1,
+ *         1 <= ctx_stride <= SV_MAX_CONTEXT, 0 <= H <= SV_MAX_CONTEXT.
+ */
+size_t sv_suffix_workspace_bytes(int32_t B, int64_t ctx_stride, int64_t H);
+int sv_suffix_propose(const int32_t *tokens, int64_t ctx_stride, const int32_t *lengths, int32_t B,
+                      const int32_t *history, int64_t H,
+                      int32_t m_min, int32_t m_max, int32_t K, double min_prob,
+                      int32_t *proposal, int32_t *proposal_len, double *score,
+                      int32_t *match_len, int32_t *source, uint32_t *flags,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sv_ngram_propose -- [Handbook] "N-gram" (take a suffix, find an earlier

@@ -12,6 +12,7 @@ the calls raise; there is no fallback path.
     verify_rejection(target, draft_logits, draft, uniforms, temperature=1.0, draft_len=None)
     verify_tree(logits, parent, token)
     ngram_propose(tokens, lengths, n_min, n_max, K)
+    suffix_propose(tokens, lengths, history, m_min, m_max, K, min_prob)
 """
 from __future__ import annotations
 
@@ -38,6 +39,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_se
            "sv_verify_greedy_partials", "sv_verify_tree_partials",
            "sv_rejection_shard_workspace_bytes", "sv_rejection_shard_stats",
            "sv_verify_rejection_partials", "sv_rejection_shard_mass", "sv_rejection_shard_sample",
+           "sv_suffix_workspace_bytes", "sv_suffix_propose",
            "sv_adaptive_init", "sv_adaptive_update")
 
 # One sv_argmax_partial: the row's largest value and the lowest global token
@@ -121,6 +123,11 @@ def load(path: str = LIB_PATH):
         L.sv_rejection_shard_sample.restype = ctypes.c_int
         L.sv_rejection_shard_sample.argtypes = [P, P, i32, i64, P, P, P, P, i32, i32, ctypes.c_float,
                                                 i32, i32, i32, i32, P, P, sz, P]
+        L.sv_suffix_workspace_bytes.restype = sz
+        L.sv_suffix_workspace_bytes.argtypes = [i32, i64, i64]
+        L.sv_suffix_propose.restype = ctypes.c_int
+        L.sv_suffix_propose.argtypes = [P, i64, P, i32, P, i64, i32, i32, i32, ctypes.c_double,
+                                        P, P, P, P, P, P, P, sz, P]
         L.sv_adaptive_init.restype = ctypes.c_int
         L.sv_adaptive_init.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
         L.sv_adaptive_update.restype = ctypes.c_int
@@ -191,6 +198,15 @@ def _logits_args(x, name, rows_dims):
         if x.stride(d) != x.size(d + 1) * x.stride(d + 1):
             raise ValueError("%s rows must be evenly spaced; call .contiguous()" % name)
     return code, rs
+
+
+def _rows_readable(t, rows, stride, name):
+    """The C calls may read every entry of every [stride] row: check that
+    the tensor's storage holds rows * stride elements from its first one."""
+    have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if have < rows * stride:
+        raise ValueError("%s: rows of stride %d need %d elements of storage from the first one, "
+                         "have %d; pass .contiguous()" % (name, stride, rows * stride, have))
 
 
 def _i32(t, shape, name):
@@ -339,6 +355,7 @@ def prepare_ngram(tokens, lengths, n_min, n_max, K):
     B = tokens.shape[0]
     stride = tokens.stride(0)
     dev = tokens.device
+    _rows_readable(tokens, B, stride, "tokens")
     _i32(lengths, (B,), "lengths")
     prop = torch.empty(B, K, dtype=torch.int32, device=dev)
     plen = torch.empty(B, dtype=torch.int32, device=dev)
@@ -354,6 +371,45 @@ def prepare_ngram(tokens, lengths, n_min, n_max, K):
 
 def ngram_propose(*a, **k):
     return prepare_ngram(*a, **k)()
+
+
+def prepare_suffix(tokens, lengths, history, m_min, m_max, K, min_prob):
+    """Suffix-decoding proposal.  tokens [B, stride] int32 (unit inner
+    stride), lengths [B] int32, history [H] int32 (contiguous) or None.
+    Outputs: proposal [B, K], proposal_len [B], score [B] float64,
+    match_len [B], source [B] (0 context, 1 history, -1 none), flags [B]."""
+    torch = _torch()
+    L = load()
+    if tokens.dtype != torch.int32 or tokens.dim() != 2 or tokens.stride(1) != 1:
+        raise ValueError("tokens must be an int32 [B, stride] tensor with unit inner stride")
+    B = tokens.shape[0]
+    stride = tokens.stride(0)
+    dev = tokens.device
+    _rows_readable(tokens, B, stride, "tokens")
+    _i32(lengths, (B,), "lengths")
+    H = 0
+    if history is not None:
+        if history.dtype != torch.int32 or history.dim() != 1 or not history.is_contiguous():
+            raise ValueError("history must be a contiguous int32 [H] tensor")
+        H = history.numel()
+    prop = torch.empty(B, K, dtype=torch.int32, device=dev)
+    plen = torch.empty(B, dtype=torch.int32, device=dev)
+    sco = torch.empty(B, dtype=torch.float64, device=dev)
+    ml = torch.empty(B, dtype=torch.int32, device=dev)
+    src = torch.empty(B, dtype=torch.int32, device=dev)
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    s = _stream(dev)
+    ws = workspace(L.sv_suffix_workspace_bytes(B, stride, H), dev, s)
+    args = (tokens.data_ptr(), stride, lengths.data_ptr(), B,
+            history.data_ptr() if H > 0 else None, H, m_min, m_max, K, float(min_prob),
+            prop.data_ptr() if K > 0 else None, plen.data_ptr(), sco.data_ptr(), ml.data_ptr(),
+            src.data_ptr(), flg.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    out = dict(proposal=prop, proposal_len=plen, score=sco, match_len=ml, source=src, flags=flg)
+    return Prepared(L.sv_suffix_propose, args, out, (tokens, lengths, history, ws))
+
+
+def suffix_propose(*a, **k):
+    return prepare_suffix(*a, **k)()
 
 
 # ---------------------------------------------------------------- vocabulary shards

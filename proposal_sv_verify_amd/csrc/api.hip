@@ -888,6 +888,93 @@ int sv_rejection_shard_sample(const void *target_logits, const void *draft_logit
     return SV_OK;
 }
 
+// ------------------------------------------------------------------ suffix
+
+namespace {
+
+int suffix_chunks(int64_t n) { return static_cast<int>((n + sv::kSfxChunk - 1) / sv::kSfxChunk); }
+
+} // namespace
+
+size_t sv_suffix_workspace_bytes(int32_t B, int64_t ctx_stride, int64_t H)
+{
+    if (B < 1 || ctx_stride < 1 || ctx_stride > SV_MAX_CONTEXT || H < 0 || H > SV_MAX_CONTEXT)
+        return 0;
+    return align_up(sizeof(sv::SuffixScanRec) * static_cast<size_t>(B) *
+                    static_cast<size_t>(suffix_chunks(ctx_stride) + suffix_chunks(H)));
+}
+
+int sv_suffix_propose(const int32_t *tokens, int64_t ctx_stride, const int32_t *lengths, int32_t B,
+                      const int32_t *history, int64_t H,
+                      int32_t m_min, int32_t m_max, int32_t K, double min_prob,
+                      int32_t *proposal, int32_t *proposal_len, double *score,
+                      int32_t *match_len, int32_t *source, uint32_t *flags,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    int st;
+    if (B < 1)
+        return fail(SV_ERR_INVALID_ARG, "B = %d < 1", B);
+    if (m_min < 1 || m_max < m_min)
+        return fail(SV_ERR_INVALID_ARG, "need 1 <= m_min <= m_max (got %d, %d)", m_min, m_max);
+    if (m_max > SV_SUFFIX_MAX_MATCH)
+        return fail(SV_ERR_UNSUPPORTED, "m_max = %d above %d", m_max, SV_SUFFIX_MAX_MATCH);
+    if (K < 0)
+        return fail(SV_ERR_INVALID_ARG, "K = %d < 0", K);
+    if (K > SV_SUFFIX_MAX_K)
+        return fail(SV_ERR_UNSUPPORTED, "K = %d above %d", K, SV_SUFFIX_MAX_K);
+    if (!(min_prob >= 0.0 && min_prob <= 1.0))
+        return fail(SV_ERR_INVALID_ARG, "min_prob must lie in [0, 1]");
+    if (ctx_stride < 1 || ctx_stride > SV_MAX_CONTEXT)
+        return fail(ctx_stride < 1 ? SV_ERR_INVALID_ARG : SV_ERR_UNSUPPORTED,
+                    "ctx_stride = %lld outside [1, %d]", static_cast<long long>(ctx_stride),
+                    SV_MAX_CONTEXT);
+    if (H < 0 || H > SV_MAX_CONTEXT)
+        return fail(H < 0 ? SV_ERR_INVALID_ARG : SV_ERR_UNSUPPORTED,
+                    "H = %lld outside [0, %d]", static_cast<long long>(H), SV_MAX_CONTEXT);
+    if (!tokens || !lengths || !proposal_len)
+        return fail(SV_ERR_INVALID_ARG, "tokens, lengths and proposal_len are required");
+    if (K > 0 && !proposal)
+        return fail(SV_ERR_INVALID_ARG, "proposal is NULL");
+    if (H > 0 && !history)
+        return fail(SV_ERR_INVALID_ARG, "history is NULL with H = %lld", static_cast<long long>(H));
+    if (score && misaligned(score, 8))
+        return fail(SV_ERR_INVALID_ARG, "score must be 8-byte aligned");
+    if ((st = check_workspace(workspace, workspace_bytes, sv_suffix_workspace_bytes(B, ctx_stride, H))) != SV_OK)
+        return st;
+    const int nch_ctx = suffix_chunks(ctx_stride), nch_hist = suffix_chunks(H);
+    if ((st = check_grid((static_cast<int64_t>(B) * (nch_ctx + nch_hist) + 3) / 4)) != SV_OK)
+        return st;
+    if ((st = check_device()) != SV_OK)
+        return st;
+
+    sv::SuffixParams p{};
+    p.tokens = tokens;
+    p.ctx_stride = ctx_stride;
+    p.lengths = lengths;
+    p.B = B;
+    p.history = H > 0 ? history : tokens;
+    p.H = H;
+    p.m_min = m_min;
+    p.m_max = m_max;
+    p.K = K;
+    p.min_prob = min_prob;
+    p.proposal = K > 0 ? proposal : proposal_len;
+    p.proposal_len = proposal_len;
+    p.score = score;
+    p.match_len = match_len;
+    p.source = source;
+    p.flags = flags;
+    p.rec = static_cast<sv::SuffixScanRec *>(workspace);
+    p.nch_ctx = nch_ctx;
+    p.nch_hist = nch_hist;
+    p.vec_ok = !misaligned(tokens, 16) && ctx_stride % 4 == 0 &&
+               (H == 0 || (!misaligned(history, 16) && H % 4 == 0));
+    hipError_t e = sv::launch_suffix(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "suffix launch");
+    return SV_OK;
+}
+
 // ------------------------------------------------------------------ n-gram
 
 int sv_ngram_propose(const int32_t *tokens, int64_t ctx_stride,

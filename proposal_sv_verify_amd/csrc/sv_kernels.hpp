@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "specverify.h"
+
 namespace sv {
 
 // Elements of one final-sample chunk in rejection sampling (16 per thread of
@@ -166,5 +168,39 @@ struct NgramParams {
 };
 
 hipError_t launch_ngram(const NgramParams &p, hipStream_t s);
+
+// Suffix decoding.  A scan item is one wave over one chunk of candidate end
+// positions of one text (the sequence's context, or the shared history) for
+// one sequence; it leaves the chunk's longest match and that match's most
+// recent occurrences.
+constexpr int kSfxChunk = 4 * 256;      // candidate ends per scan item
+
+struct SuffixScanRec {
+    int best;                    // longest match in the chunk (0: none)
+    int cnt;                     // occurrences recorded (at most SV_SUFFIX_OCC)
+    int occ[SV_SUFFIX_OCC];      // their end positions, most recent first
+};
+
+struct SuffixParams {
+    const int32_t *tokens;
+    int64_t ctx_stride;
+    const int32_t *lengths;
+    int32_t B;
+    const int32_t *history;   // a valid stand-in (tokens) when H == 0
+    int64_t H;
+    int32_t m_min, m_max, K;
+    double min_prob;
+    int32_t *proposal;        // [B][K], a stand-in when K == 0
+    int32_t *proposal_len;
+    double *score;
+    int32_t *match_len;
+    int32_t *source;
+    uint32_t *flags;
+    SuffixScanRec *rec;       // [B][nch_ctx + nch_hist]
+    int32_t nch_ctx, nch_hist;
+    int32_t vec_ok;           // 16-byte loads: aligned rows and history, ctx_stride % 4 == 0
+};
+
+hipError_t launch_suffix(const SuffixParams &p, hipStream_t s);
 
 } // namespace sv

@@ -299,3 +299,40 @@ def ngram_workload(B, L, vocab=151936, zipf_s=1.1, n_spans=8, span_min=32, span_
         for b in range(s, e):
             plant_spans(rng, toks[b], n_spans, span_min, span_max, end_at_tail=(b % 2 == 0))
     return dict(tokens=toks, lengths=np.full(B, L, np.int32), B=B, L=L)
+
+
+# Suffix decoding: the n-gram contexts, plus a shared history of earlier
+# outputs.  [Arctic] "suffix decoding" targets agent loops that regenerate
+# earlier material; the history stands in for those earlier outputs:
+# documents of Zipf background, each carrying copies of spans taken from
+# the contexts (so that a context's recent tokens can have been generated
+# before) and copies of its own earlier spans, separated by -1.
+SUFFIX = dict(B=64, L=8192, H=262144, m_min=1, m_max=32, K=16, min_prob=0.1)
+
+
+def suffix_workload(B, L, H, vocab=151936, zipf_s=1.1, seed=0, doc_min=256, doc_max=4096,
+                    copies_per_doc=4, span_min=16, span_max=256):
+    """contexts as ngram_workload(B, L); history [H] int32 of documents
+    (length U[doc_min, doc_max]) split by -1 separators."""
+    wl = ngram_workload(B, L, vocab=vocab, zipf_s=zipf_s, seed=seed)
+    rng = _rng(seed + 104729)
+    hist = zipf_tokens(rng, (H,), vocab, zipf_s).astype(np.int32)
+    pos = 0
+    while pos < H:
+        n = int(rng.integers(doc_min, doc_max + 1))
+        end = min(H, pos + n)
+        doc = hist[pos:end]
+        for _ in range(copies_per_doc):
+            ln = int(rng.integers(span_min, span_max + 1))
+            if ln >= len(doc):
+                break
+            dst = int(rng.integers(0, len(doc) - ln + 1))
+            b = int(rng.integers(0, B))
+            src = int(rng.integers(0, L - ln + 1))
+            doc[dst:dst + ln] = wl["tokens"][b, src:src + ln]
+        if end < H:
+            hist[end] = -1
+        pos = end + 1
+    wl["history"] = hist
+    wl["H"] = H
+    return wl

@@ -268,3 +268,33 @@ def test_rejection_shard_calls_reject_bad_arguments(lib):
     assert sample(wsb=8) == sv.SV_ERR_WORKSPACE
     for f in (stats, decide, mass, sample):
         assert lib.sv_last_error_message()
+
+
+def test_suffix_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(tok=FAKE, stride=64, lens=FAKE, B=2, hist=FAKE, H=100, mmin=1, mmax=8, K=4,
+                 mp=0.1, prop=FAKE, plen=FAKE, score=FAKE, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_suffix_propose(a["tok"], a["stride"], a["lens"], a["B"], a["hist"], a["H"],
+                                     a["mmin"], a["mmax"], a["K"], a["mp"], a["prop"], a["plen"],
+                                     a["score"], None, None, None, a["ws"], a["wsb"], None)
+    assert call(B=0) == sv.SV_ERR_INVALID_ARG
+    assert call(mmin=0) == sv.SV_ERR_INVALID_ARG
+    assert call(mmin=5, mmax=4) == sv.SV_ERR_INVALID_ARG
+    assert call(mmax=33) == sv.SV_ERR_UNSUPPORTED
+    assert call(K=-1) == sv.SV_ERR_INVALID_ARG
+    assert call(K=33) == sv.SV_ERR_UNSUPPORTED
+    assert call(mp=-0.1) == sv.SV_ERR_INVALID_ARG
+    assert call(mp=1.5) == sv.SV_ERR_INVALID_ARG
+    assert call(mp=float("nan")) == sv.SV_ERR_INVALID_ARG
+    assert call(stride=0) == sv.SV_ERR_INVALID_ARG
+    assert call(stride=(1 << 26) + 1) == sv.SV_ERR_UNSUPPORTED
+    assert call(H=-1) == sv.SV_ERR_INVALID_ARG
+    assert call(hist=None) == sv.SV_ERR_INVALID_ARG            # H > 0 needs a history
+    assert call(prop=None) == sv.SV_ERR_INVALID_ARG
+    assert call(plen=None) == sv.SV_ERR_INVALID_ARG
+    assert call(score=FAKE + 4) == sv.SV_ERR_INVALID_ARG
+    assert call(wsb=8) == sv.SV_ERR_WORKSPACE
+    assert lib.sv_last_error_message()
+    assert lib.sv_suffix_workspace_bytes(0, 64, 0) == 0
+    assert lib.sv_suffix_workspace_bytes(64, 8192, 262144) > 64 * 17 * 1024
