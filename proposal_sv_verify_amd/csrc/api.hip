@@ -640,6 +640,7 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     p.seg_len = pl.seg_len;
     p.part_row_step = pl.segs;
     p.part_seg_step = 1;
+    p.capture_x = 1;
     set_temperature(p, temperature);
     p.draft = K > 0 ? draft : accepted;
     p.draft_len = draft_len ? draft_len : accepted;

@@ -17,12 +17,13 @@
 // (reference, sum).
 //
 // Kernel 2 (accept scan).  One workgroup per sequence: merge the segment
-// statistics of each row in LDS, then one lane per draft position computes
+// statistics of each row in LDS, with the logits at the draft tokens that
+// the statistics kernel captured, then one lane per draft position computes
 // p_k(x_k) and q_k(x_k) with fp64 exp and the test u_k < p/q in fp64; a
 // ballot of the rejections gives the first one, n.  The lane at position n
 // publishes the statistics of row pair n.  (Running this inside kernel 3's
-// workgroups instead was measured slower: every chunk then waits out the
-// whole decision before loading its data.)
+// workgroups instead was measured slower, 18.5-19.7 us against 5 + 9.6 us:
+// every chunk then waits out the whole decision before loading its data.)
 //
 // Kernel 3 (final-sample masses).  The final token is drawn from one row
 // pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const float inv_t = p.inv_t;
         const double inv_t_d = p.inv_t_d;
         const float c1 = p.split_c1, k2 = p.split_k2;
-        stream_segment<E, 4, 64>(
+        stream_segment<E, 4, 64, true>(
             rp, lo, hi, lane,
             [&](const float(&f)[Elem<E>::kPerVec], int) {
                 const float s = vec_exp_sum<kMode>(f, inv_t, c1, k2);
@@ -276,8 +277,9 @@ __global__ __launch_bounds__(kThreads) void k_rej_shard_rows(const RejectParams 
 // draft row base + i at slot D0 + i, D0 = min(64, K + 1): for K < 64 the rows
 // are packed (2K + 1 of them).  With `publish` the workgroup also writes the
 // call's per-sequence outputs and the sequence state; every thread gets the
-// state back.  kShardIn: the "segments" are vocabulary shards, and the logits
-// at the draft tokens come with the partials instead of from the rows.
+// state back.  The logits at the draft tokens come with the partials (the
+// statistics kernel captures them); the "segments" are a row's pieces, or
+// its vocabulary shards.
 constexpr int kScanRows = 128;                                 // LDS row slots, at most
 constexpr int kScanPer = kScanRows * kMaxSegs / kThreads;      // partials per thread, at most
 
@@ -310,7 +312,6 @@ struct ScanLds {
     }
 };
 
-template <typename E, bool kShardIn>
 __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool publish, const ScanLds &S,
                                            int &len_out)
 {
@@ -346,11 +347,7 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
         }
         const bool valid = K > 0 && x >= 0 && x < p.v_full;
         const int xc = valid ? x : 0;
-        float lt = 0.0f, ld = 0.0f;
-        if constexpr (!kShardIn) {
-            lt = Elem<E>::one(static_cast<const E *>(p.target) + (static_cast<int64_t>(b) * (K + 1) + kc) * p.row_stride, xc);
-            ld = Elem<E>::one(static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + kc) * p.row_stride, xc);
-        }
+        (void)xc;
         const int len_raw = p.draft_len[b];
         len = p.has_len ? clamp_len(len_raw, K, fl) : K;
 #pragma unroll
@@ -365,8 +362,7 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
                 const int slot = (tgt ? rc : D0 + rc - nt) * segs + s;
                 S.m[slot] = use ? q[j].m : -__builtin_inff();
                 S.z[slot] = use ? q[j].z : 0.0;
-                if (kShardIn)
-                    S.lxs[slot] = use ? q[j].lx : __builtin_nanf("");
+                S.lxs[slot] = use ? q[j].lx : __builtin_nanf("");
             }
         }
         __syncthreads();
@@ -376,15 +372,12 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             float l = __builtin_nanf("");
             for (int s = 0; s < segs; ++s) {
                 M = fmaxf(M, S.m[srow * segs + s]);
-                if (kShardIn) {
-                    const float c = S.lxs[srow * segs + s];
-                    if (c == c)
-                        l = c;
-                }
+                const float c = S.lxs[srow * segs + s];
+                if (c == c)
+                    l = c;
             }
             S.M[srow] = M;
-            if (kShardIn)
-                S.lx[srow] = l;
+            S.lx[srow] = l;
         }
         __syncthreads();
         for (int ci = t; ci < cnt; ci += kThreads) {
@@ -410,10 +403,8 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             const bool has_t = lane < nt, has_d = lane < nd;
             const double zt = has_t ? S.Z[lane] : 0.0, zd = has_d ? S.Z[D0 + lane] : 0.0;
             const float mt = has_t ? S.M[lane] : 0.0f, md = has_d ? S.M[D0 + lane] : 0.0f;
-            if (kShardIn) {
-                lt = has_t ? S.lx[lane] : 0.0f;
-                ld = has_d ? S.lx[D0 + lane] : 0.0f;
-            }
+            const float lt = has_t ? S.lx[lane] : 0.0f;
+            const float ld = has_d ? S.lx[D0 + lane] : 0.0f;
             double pk = 0.0, qk = 0.0;
             bool rejected = false;
             if (k < len) {
@@ -479,14 +470,13 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
     return *S.seq;                            // written before the last barrier
 }
 
-// Kernel 2: one workgroup per sequence.
-template <typename E, bool kShardIn>
+// Kernel 2: the accept decision, one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
 {
     extern __shared__ __align__(16) char s_dyn[];
     const ScanLds S(s_dyn, p.K, p.segs);
     int len;
-    decide<E, kShardIn>(p, blockIdx.x, true, S, len);
+    decide(p, blockIdx.x, true, S, len);
 }
 
 // kN consecutive elements [v0, v0 + kN) of a row, loaded before use.  kVec:
@@ -616,8 +606,9 @@ __device__ __forceinline__ void chunk_masses(const RejectParams &p, int b, int c
             ChunkMass{rs, ps};
 }
 
-// Kernel 3: one workgroup per (sequence, chunk); two memory rounds (the
-// sequence state, then both rows' slices).
+// Kernel 3: final-sample masses, one workgroup per (sequence, chunk), on
+// the sequence state of the accept decision: two memory rounds (the state,
+// then both rows' slices).
 template <typename E, bool kVec>
 __global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
 {
@@ -831,7 +822,7 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
     if (e != hipSuccess)
         return e;
     const size_t lds = scan_lds_bytes(p.K, p.segs);
-    hipLaunchKernelGGL((k_rej_scan<E, false>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL(k_rej_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
@@ -899,7 +890,7 @@ hipError_t launch_rejection_shard_stats(const RejectParams &p, int dtype, SoftPa
 hipError_t launch_rejection_decide(const RejectParams &p, hipStream_t s)
 {
     const size_t lds = scan_lds_bytes(p.K, p.segs);
-    hipLaunchKernelGGL((k_rej_scan<float, true>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL(k_rej_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
     return hipGetLastError();
 }
 

@@ -54,6 +54,12 @@ __device__ __forceinline__ u32x4 load16(const u32x4 *p)
     return __builtin_nontemporal_load(p);
 }
 
+// A 16-byte load with the default cache policy, for data read again soon.
+__device__ __forceinline__ u32x4 load16_keep(const u32x4 *p)
+{
+    return *p;
+}
+
 // Visit elements [lo, hi) of one row with kSpan cooperating threads (a
 // workgroup, or one wave); t is this thread's index among them.  Each thread
 // sees its elements in increasing index order: one unaligned head element,
@@ -65,9 +71,10 @@ __device__ __forceinline__ u32x4 load16(const u32x4 *p)
 // processed and the thread only ever waits for its oldest load.  Loads past the last vector are
 // clamped onto it (every load is issued unconditionally, which keeps the
 // compiler's wait counts exact) and their data is dropped.
-template <typename E, int kDepth, int kSpan, typename FV, typename F1>
+template <typename E, int kDepth, int kSpan, bool kKeep = false, typename FV, typename F1>
 __device__ __forceinline__ void stream_segment(const E *row, int lo, int hi, int t, FV &&fvec, F1 &&fone)
 {
+    auto ld = [](const u32x4 *p) { return kKeep ? load16_keep(p) : load16(p); };
     constexpr int PV = Elem<E>::kPerVec;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(row + lo);
     int head = static_cast<int>(((16u - (addr & 15u)) & 15u) / sizeof(E));
@@ -83,7 +90,7 @@ __device__ __forceinline__ void stream_segment(const E *row, int lo, int hi, int
         u32x4 q[kDepth];
 #pragma unroll
         for (int u = 0; u < kDepth; ++u)
-            q[u] = load16(vp + min(t + u * kSpan, last));
+            q[u] = ld(vp + min(t + u * kSpan, last));
         for (int v = t; v < nvec; v += kDepth * kSpan) {
 #pragma unroll
             for (int u = 0; u < kDepth; ++u) {
@@ -93,7 +100,7 @@ __device__ __forceinline__ void stream_segment(const E *row, int lo, int hi, int
                     Elem<E>::unpack(q[u], f);
                     fvec(f, a + vi * PV);
                 }
-                q[u] = load16(vp + min(vi + kDepth * kSpan, last));
+                q[u] = ld(vp + min(vi + kDepth * kSpan, last));
             }
         }
     }
