@@ -11,8 +11,9 @@
 // m(e) >= n_min.
 //
 // kW waves work on one context (kW = 1 for many contexts, so that each
-// wave's in-flight reads are few at its early exit; kW = 4 for few, so that
-// a context is scanned four tiles at a time).  Wave `sub` scores the
+// wave's in-flight reads are few at its early exit; kW = 4 or 16 for fewer,
+// so that a context is scanned that many tiles at a time: with 16 waves a
+// 8192-token context is in flight in one round).  Wave `sub` scores the
 // 256-position tiles t_top - sub, t_top - sub - kW, ... from the end of the
 // context backwards; each tile comes with the 32 positions below it (the
 // longest comparison's reach), through a ring of kDepth loads per lane, so
@@ -60,19 +61,20 @@ __device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int stride)
     }
 }
 
-template <bool kVec, int kW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_ngram(const NgramParams p)
+template <bool kVec, int kW, int kWG>
+__global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8))) void k_ngram(const NgramParams p)
 {
-    static_assert(kWaves % kW == 0, "whole contexts per workgroup");
-    __shared__ int s_buf[kWaves][kHalo + kTile];  // a wave's tile, halo below it
-    __shared__ int s_suf[kWaves][64];             // s_suf[j] = c[L-1-j] for j < n_max
-    __shared__ int s_full[kWaves / kW];           // highest tile with a full-length match
-    __shared__ int s_key[kWaves];
+    constexpr int kWv = kWG / 64;                 // waves per workgroup
+    static_assert(kWv % kW == 0, "whole contexts per workgroup");
+    __shared__ int s_buf[kWv][kHalo + kTile];     // a wave's tile, halo below it
+    __shared__ int s_suf[kWv][64];                // s_suf[j] = c[L-1-j] for j < n_max
+    __shared__ int s_full[kWv / kW];              // highest tile with a full-length match
+    __shared__ int s_key[kWv];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int sub = w % kW;
     const int slot = w / kW;
-    const int b = blockIdx.x * (kWaves / kW) + slot;
+    const int b = blockIdx.x * (kWv / kW) + slot;
     const bool live = b < p.B;                    // uniform over the context's waves
     const int stride = static_cast<int>(p.ctx_stride);
     const int32_t *c = p.tokens + static_cast<int64_t>(live ? b : 0) * p.ctx_stride;
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
     const int nmax = p.n_max, nmin = p.n_min;
     if (kW > 1) {
-        if (threadIdx.x < kWaves / kW)
+        if (threadIdx.x < kWv / kW)
             s_full[threadIdx.x] = -1;
         __syncthreads();
     }
@@ -211,12 +213,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     }
 }
 
-template <bool kVec, int kW>
+template <bool kVec, int kW, int kWG>
 hipError_t launch_w(const NgramParams &p, hipStream_t s)
 {
-    constexpr int kPerWg = kWaves / kW;
-    hipLaunchKernelGGL((k_ngram<kVec, kW>), dim3(static_cast<unsigned>((p.B + kPerWg - 1) / kPerWg)),
-                       dim3(kThreads), 0, s, p);
+    constexpr int kPerWg = kWG / 64 / kW;
+    hipLaunchKernelGGL((k_ngram<kVec, kW, kWG>), dim3(static_cast<unsigned>((p.B + kPerWg - 1) / kPerWg)),
+                       dim3(kWG), 0, s, p);
     return hipGetLastError();
 }
 
@@ -225,11 +227,14 @@ hipError_t launch_w(const NgramParams &p, hipStream_t s)
 hipError_t launch_ngram(const NgramParams &p, hipStream_t s)
 {
     // one wave per context once the contexts alone fill the chip's wave slots
-    // (256 CUs x 32) twice; four waves per context below that
-    const bool many = p.B >= 2 * 256 * 32;
+    // (256 CUs x 32) twice; four waves per context below that, and sixteen
+    // (one 1024-thread workgroup) for a batch of at most 512 contexts
+    const bool many = p.B >= 2 * 256 * 32, few = p.B <= 512;
     if (p.vec_ok)
-        return many ? launch_w<true, 1>(p, s) : launch_w<true, 4>(p, s);
-    return many ? launch_w<false, 1>(p, s) : launch_w<false, 4>(p, s);
+        return many ? launch_w<true, 1, kThreads>(p, s)
+                    : (few ? launch_w<true, 16, 1024>(p, s) : launch_w<true, 4, kThreads>(p, s));
+    return many ? launch_w<false, 1, kThreads>(p, s)
+                : (few ? launch_w<false, 16, 1024>(p, s) : launch_w<false, 4, kThreads>(p, s));
 }
 
 } // namespace sv
