@@ -113,9 +113,31 @@ __device__ __forceinline__ void score_chunk(const int *buf, const int *sfx, int 
             const int64_t e = lo + (o - kHalo);
             int m = 0;
             if (buf[o] == s0 && e >= e_lo && e <= e_hi && buf[o + 1] >= 0) {
+                // one step, then (for the rare long matches) four steps per
+                // round: eight independent LDS reads, one wait (reads past
+                // m_max are clamped into the buffer and unused)
                 m = 1;
-                while (m < m_max && e - m >= 0 && sfx[m] >= 0 && buf[o - m] == sfx[m])
-                    ++m;
+                if (m < m_max && e - 1 >= 0 && sfx[1] >= 0 && buf[o - 1] == sfx[1]) {
+                    m = 2;
+                    for (;;) {
+                        int t[4], pt[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            t[j] = buf[max(o - m - j, 0)];
+                            pt[j] = sfx[min(m + j, kHalo - 1)];
+                        }
+                        int adv = 0;
+                        bool run = true;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            run = run && m + j < m_max && e - m - j >= 0 && pt[j] >= 0 && t[j] == pt[j];
+                            adv += run ? 1 : 0;
+                        }
+                        m += adv;
+                        if (adv < 4)
+                            break;
+                    }
+                }
                 if (m < m_min)
                     m = 0;
             }
