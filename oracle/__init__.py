@@ -21,6 +21,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+PROBS = 2
 
 FLAG_DRAFT_OOR = 1
 FLAG_BAD_LEN = 2
@@ -125,9 +126,10 @@ class Oracle:
 
     def verify_rejection(self, target, draft_logits, draft, uniforms, temperature=1.0,
                          draft_len=None, accept_band=ACCEPT_BAND,
-                         sample_band_scale=SAMPLE_BAND_SCALE):
+                         sample_band_scale=SAMPLE_BAND_SCALE, probs=False):
         """target [B, K+1, V], draft_logits [B, K, V], draft [B, K],
-        uniforms [B, K+1] float32."""
+        uniforms [B, K+1] float32.  probs: the rows are float32
+        probabilities (each row divided by its sum; temperature unused)."""
         target = np.ascontiguousarray(target)
         draft_logits = np.ascontiguousarray(draft_logits)
         B, K1, V = target.shape
@@ -144,7 +146,10 @@ class Oracle:
         at = np.zeros(B, np.uint8)
         st = np.zeros(B, np.uint8)
         flg = np.zeros(B, np.uint32)
-        self.lib.orc_verify_rejection(_ptr(target), _ptr(draft_logits), _dtype_code(target), V,
+        if probs and target.dtype != np.float32:
+            raise TypeError("probabilities must be float32")
+        code = PROBS if probs else _dtype_code(target)
+        self.lib.orc_verify_rejection(_ptr(target), _ptr(draft_logits), code, V,
                                       _ptr(draft), _ptr(draft_len), _ptr(u), float(temperature),
                                       B, K, V, float(accept_band), float(sample_band_scale),
                                       _ptr(acc), _ptr(emi), _ptr(pd), _ptr(qd), _ptr(at),

@@ -18,7 +18,7 @@
 /* bf16 is the top half of an IEEE binary32; widening is a 16-bit shift. */
 double orc_widen(const void *row, int dtype, int64_t i)
 {
-    if (dtype == ORC_F32)
+    if (dtype == ORC_F32 || dtype == ORC_PROBS)
         return (double)((const float *)row)[i];
     uint32_t bits = ((uint32_t)((const uint16_t *)row)[i]) << 16;
     float f;
@@ -28,7 +28,7 @@ double orc_widen(const void *row, int dtype, int64_t i)
 
 static const void *row_ptr(const void *base, int dtype, int64_t row, int64_t row_stride)
 {
-    size_t esize = dtype == ORC_F32 ? 4 : 2;
+    size_t esize = dtype == ORC_BF16 ? 2 : 4;
     return (const char *)base + (size_t)row * (size_t)row_stride * esize;
 }
 
@@ -115,6 +115,14 @@ void orc_verify_greedy(const void *logits, int dtype, int64_t row_stride,
  *   z_v = l_v / T,  M = max_v z_v,  p_v = exp(z_v - M) / sum_w exp(z_w - M). */
 static void softmax_row(const void *row, int dtype, int32_t V, double T, double *p)
 {
+    if (dtype == ORC_PROBS) {          /* given probabilities: normalise the row */
+        double Z = 0.0;
+        for (int32_t v = 0; v < V; ++v)
+            Z += orc_widen(row, dtype, v);
+        for (int32_t v = 0; v < V; ++v)
+            p[v] = orc_widen(row, dtype, v) / Z;
+        return;
+    }
     double M = -INFINITY;
     for (int32_t v = 0; v < V; ++v) {
         double z = orc_widen(row, dtype, v) / T;

@@ -46,6 +46,7 @@ extern "C" {
 /* input element types */
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_PROBS 2    /* rejection sampling only: fp32 rows of probabilities */
 
 /* per-sequence data-error flag bits (same meaning as the library's) */
 #define ORC_FLAG_DRAFT_OOR 1u    /* a draft / node token id outside [0, V) */
@@ -76,6 +77,9 @@ void orc_verify_greedy(const void *logits, int dtype, int64_t row_stride,
  * target [B][K+1][row_stride], draftl [B][K][row_stride], draft [B][K],
  * draft_len [B] or NULL, u [B][K+1] in [0,1): u[b][i] drives accept test i,
  * u[b][K] drives the one final sample.  T > 0 is applied to both models.
+ * dtype ORC_PROBS: the rows hold probabilities (fp32, non-negative, each
+ * row with a positive sum); a row's distribution is the row over its sum,
+ * and T is not used.
  * Outputs: accepted [B], emitted [B][K+1] (-1 padded),
  *   p_draft / q_draft [B][K] (p_i(x_i), q_i(x_i) for i < draft_len and a
  *   valid id, else 0) or NULL,

@@ -73,6 +73,9 @@ MUTANTS = [
      "pr[k] = c[got_s + k];", NGRAM_PINS),
     ("n-gram lets the suffix match itself", "for (int64_t s = L - n - 1; s >= 0; --s) {",
      "for (int64_t s = L - n; s >= 0; --s) {", NGRAM_PINS),
+    ("given probabilities are not normalised", "p[v] = orc_widen(row, dtype, v) / Z;",
+     "p[v] = orc_widen(row, dtype, v);",
+     [R.test_probability_input_equals_logit_input, lambda o: R.test_probability_input_chisquare_v8(o, 1)]),
     ("suffix counts the oldest occurrences",
      "for (int64_t e = len_t - 2; e >= 0 && n < occ_cap; --e)",
      "for (int64_t e = 0; e <= len_t - 2 && n < occ_cap; ++e)", SUFFIX_PINS),

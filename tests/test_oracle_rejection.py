@@ -219,3 +219,73 @@ def test_masked_entries_equal_smaller_vocabulary(orc):
             n = small["accepted"][b]
             np.testing.assert_array_equal(large["emitted"][b, :n + 1], ids[small["emitted"][b, :n + 1]])
             assert (large["emitted"][b, n + 1:] == -1).all()
+
+
+# ------------------------------------------------------- probability input
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_probability_input_chisquare_v8(orc, K):
+    """With the target and draft given as probabilities (the north-star
+    interface takes logits or probabilities), the emitted token at each
+    reached position is distributed as p and the accept frequency is
+    sum_x min(p, q); rows need not be normalised (the row's sum divides)."""
+    rng = np.random.default_rng(300 + K)
+    V, T = 8, 200_000
+    p = rng.dirichlet(np.ones(V), size=K + 1).astype(np.float32)
+    q = rng.dirichlet(np.ones(V), size=K).astype(np.float32)
+    p[0, 3] = 0.0                                  # an impossible target token
+    q[0, 5] = 0.0                                  # and an impossible draft token
+    p3 = (p * np.float32(3.0)).astype(np.float32)                         # unnormalised
+    p_eff = p3.astype(np.float64) / p3.astype(np.float64).sum(axis=1, keepdims=True)
+    q_eff = q.astype(np.float64) / q.astype(np.float64).sum(axis=1, keepdims=True)
+    target = np.broadcast_to(p3, (T, K + 1, V)).copy()
+    draftp = np.broadcast_to(q, (T, K, V)).copy()
+    x = _sample_rows(rng, q_eff, T)
+    u = rng.random((T, K + 1), dtype=np.float32)
+    out = orc.verify_rejection(target, draftp, x, u, probs=True)
+    n = out["accepted"]
+    for j in range(K + 1):
+        reached = n >= j
+        counts = np.bincount(out["emitted"][reached, j], minlength=V)
+        assert counts[3] == 0 or j != 0
+        expect = p_eff[j] * reached.sum()
+        live = expect > 0
+        assert stats.chisquare(counts[live], expect[live]).pvalue > 1e-3
+    for i in range(K):
+        reached = n >= i
+        acc = (n[reached] > i).astype(np.float64)
+        beta = np.minimum(p_eff[i], q_eff[i]).sum()
+        assert abs(acc.mean() - beta) < 4 * np.sqrt(beta * (1 - beta) / reached.sum())
+    np.testing.assert_allclose(out["p_draft"], p_eff[np.arange(K), x], rtol=1e-12)
+
+
+def test_probability_input_equals_logit_input(orc):
+    """Probabilities exp(l) / sum exp(l) rounded to fp32 give the logit
+    path's decisions except within the rounding band of a tie; scaling
+    every row by a power of two changes nothing at all."""
+    from proposal_sv_verify_amd import workloads as W
+    wl = W.rejection_workload(64, 4, 500, 1.0, 0.5, 1.0, seed=311, dtype="f32")
+    P = _softmax64(wl["target"]).astype(np.float32)
+    Q = _softmax64(wl["draft_logits"]).astype(np.float32)
+    a = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], wl["uniforms"])
+    b = orc.verify_rejection(P, Q, wl["draft"], wl["uniforms"], probs=True)
+    tie = a["accept_tie"] | a["sample_tie"] | b["accept_tie"] | b["sample_tie"]
+    same = (a["emitted"] == b["emitted"]).all(axis=1)
+    assert (same | tie).all() and same.sum() >= 60
+    c = orc.verify_rejection(P * np.float32(0.25), Q * np.float32(8.0), wl["draft"], wl["uniforms"],
+                             probs=True)
+    for k in ("accepted", "emitted", "p_draft", "q_draft", "accept_tie", "sample_tie"):
+        np.testing.assert_array_equal(b[k], c[k], err_msg=k)
+
+
+def test_probability_input_zero_draft_probability_accepts(orc):
+    """q(x) = 0 makes the ratio infinite: the draft is accepted whatever u."""
+    V = 6
+    p = np.array([[0.1, 0.2, 0.3, 0.4, 0.0, 0.0], [0.5, 0.5, 0, 0, 0, 0]], np.float32)[None]
+    q = np.array([[0.0, 0.5, 0.5, 0.0, 0.0, 0.0]], np.float32)[None]
+    x = np.array([[0]], np.int32)
+    u = np.array([[0.999, 0.7]], np.float32)
+    out = orc.verify_rejection(p, q, x, u, probs=True)
+    assert out["accepted"][0] == 1 and out["emitted"][0, 0] == 0
+    assert out["emitted"][0, 1] == 1                 # bonus from p_1 = (0.5, 0.5): u 0.7 -> id 1
+    assert V == p.shape[-1]
