@@ -185,6 +185,27 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sv_verify_rejection_probs -- sv_verify_rejection on given probabilities
+ * (the interface takes the models' logits or their probabilities): the
+ * rows are fp32, non-negative, each needed row with a positive finite sum;
+ * a row's distribution is the row divided by its sum (rows need not be
+ * normalised) and no temperature applies.  The same steps, layout,
+ * outputs, workspace (sv_rejection_workspace_bytes) and limits as
+ * sv_verify_rejection with dtype SV_F32; p_draft and q_draft report the
+ * normalised values at the drafted ids.  (Greedy and tree verification
+ * take probabilities as they are: the argmax is the same.)
+ */
+int sv_verify_rejection_probs(const float *target_probs, const float *draft_probs,
+                              int64_t row_stride,
+                              const int32_t *draft, const int32_t *draft_len,
+                              const float *uniforms,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t *accepted, int32_t *emitted,
+                              float *p_draft, float *q_draft,
+                              uint32_t *flags, int64_t *stats,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sv_verify_tree -- [Handbook] "Medusa": candidate continuations form a
  * tree scored in one pass; the longest accepted candidate prefix is kept.
  *   t_j = argmax logits[b][j] (row j scores the children of node j);

@@ -33,7 +33,7 @@ TUNE_TARGET_WORKGROUPS, TUNE_MIN_SEGMENT_BYTES = 1, 2
 # every symbol include/specverify.h declares
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_set_tuning",
            "sv_greedy_workspace_bytes", "sv_verify_greedy",
-           "sv_rejection_workspace_bytes", "sv_verify_rejection",
+           "sv_rejection_workspace_bytes", "sv_verify_rejection", "sv_verify_rejection_probs",
            "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose",
            "sv_argmax_shard_workspace_bytes", "sv_argmax_shard",
            "sv_verify_greedy_partials", "sv_verify_tree_partials",
@@ -99,6 +99,9 @@ def load(path: str = LIB_PATH):
         L.sv_verify_rejection.restype = ctypes.c_int
         L.sv_verify_rejection.argtypes = [P, P, i32, i64, P, P, P, ctypes.c_float, i32, i32, i32,
                                           P, P, P, P, P, P, P, sz, P]
+        L.sv_verify_rejection_probs.restype = ctypes.c_int
+        L.sv_verify_rejection_probs.argtypes = [P, P, i64, P, P, P, i32, i32, i32, P, P, P, P, P, P,
+                                                P, sz, P]
         L.sv_verify_tree.restype = ctypes.c_int
         L.sv_verify_tree.argtypes = [P, i32, i64, P, P, i32, i32, i32, P, P, P, P, P, P, sz, P]
         L.sv_ngram_propose.restype = ctypes.c_int
@@ -312,6 +315,51 @@ def prepare_rejection(target, draft_logits, draft, uniforms, temperature=1.0, dr
 
 def verify_rejection(*a, **k):
     return prepare_rejection(*a, **k)()
+
+
+def prepare_rejection_probs(target_probs, draft_probs, draft, uniforms, draft_len=None, *,
+                            want_probs=True, stats=None):
+    """Rejection sampling on given probabilities: target_probs [B, K+1, V]
+    and draft_probs [B, K, V] float32 (each row over its sum; no
+    temperature).  Outputs as prepare_rejection."""
+    torch = _torch()
+    L = load()
+    if target_probs.dtype != torch.float32:
+        raise TypeError("probabilities must be float32")
+    _, rs = _logits_args(target_probs, "target_probs", 2)
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = target_probs.device
+    if K > 0:
+        _, rs2 = _logits_args(draft_probs, "draft_probs", 2)
+        if draft_probs.dtype != torch.float32 or rs2 != rs or tuple(draft_probs.shape) != (B, K, V):
+            raise ValueError("draft_probs must be float32 [B, K, V] with the target's row stride")
+    _i32(draft, (B, K), "draft")
+    _i32(draft_len, (B,), "draft_len")
+    if uniforms.dtype != torch.float32 or not uniforms.is_contiguous() or \
+            tuple(uniforms.shape) != (B, K1):
+        raise ValueError("uniforms must be a contiguous float32 tensor [B, K+1]")
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 3 + K):
+        raise ValueError("stats must be an int64 tensor of at least 3+K entries")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    emi = torch.empty(B, K1, dtype=torch.int32, device=dev)
+    pd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    qd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
+    flg = torch.empty(B, dtype=torch.int32, device=dev)
+    s = _stream(dev)
+    ws = workspace(L.sv_rejection_workspace_bytes(B, K, V), dev, s)
+    args = (target_probs.data_ptr(), _ptr(draft_probs) if K > 0 else None, rs, _ptr(draft),
+            _ptr(draft_len), uniforms.data_ptr(), B, K, V, acc.data_ptr(), emi.data_ptr(), _ptr(pd),
+            _ptr(qd), flg.data_ptr(), _ptr(stats), ws.data_ptr(), ws.numel(), s)
+    out = dict(accepted=acc, emitted=emi, flags=flg)
+    if want_probs:
+        out["p_draft"], out["q_draft"] = pd, qd
+    return Prepared(L.sv_verify_rejection_probs, args, out,
+                    (target_probs, draft_probs, draft, draft_len, uniforms, stats, ws))
+
+
+def verify_rejection_probs(*a, **k):
+    return prepare_rejection_probs(*a, **k)()
 
 
 def prepare_tree(logits, parent, token, *, want_argmax=True):

@@ -596,15 +596,17 @@ size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V)
     return x > y ? x : y;
 }
 
-int sv_verify_rejection(const void *target_logits, const void *draft_logits,
-                        int32_t dtype, int64_t row_stride,
-                        const int32_t *draft, const int32_t *draft_len,
-                        const float *uniforms, float temperature,
-                        int32_t B, int32_t K, int32_t V,
-                        int32_t *accepted, int32_t *emitted,
-                        float *p_draft, float *q_draft,
-                        uint32_t *flags, int64_t *stats,
-                        void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+int rejection_call(const void *target_logits, const void *draft_logits,
+                   int32_t dtype, int64_t row_stride,
+                   const int32_t *draft, const int32_t *draft_len,
+                   const float *uniforms, float temperature,
+                   int32_t B, int32_t K, int32_t V,
+                   int32_t *accepted, int32_t *emitted,
+                   float *p_draft, float *q_draft,
+                   uint32_t *flags, int64_t *stats,
+                   void *workspace, size_t workspace_bytes, void *stream, bool probs)
 {
     int st;
     if ((st = check_sizes(B, K, V)) != SV_OK)
@@ -655,10 +657,43 @@ int sv_verify_rejection(const void *target_logits, const void *draft_logits,
     p.partial = at<sv::SoftPartial>(workspace, L.partial);
     p.seq = at<sv::SeqState>(workspace, L.seq);
     p.cmass = at<sv::ChunkMass>(workspace, L.cmass);
+    p.probs = probs;
     hipError_t e = sv::launch_rejection(p, dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "rejection launch");
     return SV_OK;
+}
+
+} // namespace
+
+int sv_verify_rejection(const void *target_logits, const void *draft_logits,
+                        int32_t dtype, int64_t row_stride,
+                        const int32_t *draft, const int32_t *draft_len,
+                        const float *uniforms, float temperature,
+                        int32_t B, int32_t K, int32_t V,
+                        int32_t *accepted, int32_t *emitted,
+                        float *p_draft, float *q_draft,
+                        uint32_t *flags, int64_t *stats,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return rejection_call(target_logits, draft_logits, dtype, row_stride, draft, draft_len, uniforms,
+                          temperature, B, K, V, accepted, emitted, p_draft, q_draft, flags, stats,
+                          workspace, workspace_bytes, stream, false);
+}
+
+int sv_verify_rejection_probs(const float *target_probs, const float *draft_probs,
+                              int64_t row_stride,
+                              const int32_t *draft, const int32_t *draft_len,
+                              const float *uniforms,
+                              int32_t B, int32_t K, int32_t V,
+                              int32_t *accepted, int32_t *emitted,
+                              float *p_draft, float *q_draft,
+                              uint32_t *flags, int64_t *stats,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    return rejection_call(target_probs, draft_probs, SV_F32, row_stride, draft, draft_len, uniforms,
+                          1.0f, B, K, V, accepted, emitted, p_draft, q_draft, flags, stats,
+                          workspace, workspace_bytes, stream, true);
 }
 
 // ------------------------------------------------------- rejection, sharded

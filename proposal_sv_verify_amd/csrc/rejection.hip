@@ -123,6 +123,7 @@ enum ExpMode : int {
     kExpUnitT = 0,    // compensated exp of l (T == 1)
     kExpScaled = 1,   // compensated exp of l * (1/T)
     kExpSplit = 2,    // bf16 only: split constant, first-order correction summed apart
+    kProbs = 3,       // the values are probabilities: summed as they are
 };
 
 // Sum of e^(f_j / T) over a vector, in fp32.  kExpSplit: with log2(e)/T =
@@ -134,7 +135,13 @@ enum ExpMode : int {
 template <int kMode, int n>
 __device__ __forceinline__ float vec_exp_sum(const float (&f)[n], float inv_t, float c1, float k2)
 {
-    if constexpr (kMode == kExpSplit) {
+    if constexpr (kMode == kProbs) {
+        float s = f[0];
+#pragma unroll
+        for (int j = 1; j < n; ++j)
+            s += f[j];
+        return s;
+    } else if constexpr (kMode == kExpSplit) {
         float e = __builtin_amdgcn_exp2f(f[0] * c1);
         float s1 = e, s2 = e * f[0];
 #pragma unroll
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
             rp, lo, hi, lane,
             [&](const float(&f)[Elem<E>::kPerVec], int) {
                 const float s = vec_exp_sum<kMode>(f, inv_t, c1, k2);
-                if (s >= kTiny && s <= kBig)
+                if (kMode == kProbs || (s >= kTiny && s <= kBig))
                     ls.z0 += static_cast<double>(s);
                 else
                     careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
             [&](float x, int) {
                 const float f1[1] = {x};
                 const float s = vec_exp_sum<kMode>(f1, inv_t, c1, k2);
-                if (s >= kTiny && s <= kBig) {
+                if (kMode == kProbs || (s >= kTiny && s <= kBig)) {
                     ls.z0 += static_cast<double>(s);
                 } else {
                     careful_add<kUnitT>(f1, s, ls, inv_t, inv_t_d);
@@ -410,8 +417,13 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
             if (k < len) {
                 double ratio = 0.0;
                 if (valid) {
-                    pk = exp((static_cast<double>(lt) - static_cast<double>(mt)) * p.inv_t_d) / zt;
-                    qk = exp((static_cast<double>(ld) - static_cast<double>(md)) * p.inv_t_d) / zd;
+                    if (p.probs) {              // given probabilities: value over the row's sum
+                        pk = static_cast<double>(lt) / zt;
+                        qk = static_cast<double>(ld) / zd;
+                    } else {
+                        pk = exp((static_cast<double>(lt) - static_cast<double>(mt)) * p.inv_t_d) / zt;
+                        qk = exp((static_cast<double>(ld) - static_cast<double>(md)) * p.inv_t_d) / zd;
+                    }
                     ratio = qk > 0.0 ? pk / qk : __builtin_inf();
                 }
                 rejected = !(static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]) < ratio);
@@ -535,6 +547,7 @@ struct SampleRows {
     const E *pt;
     const E *pd;        // the target row again when sampling the bonus
     bool residual;      // a draft row is present: r is formed
+    bool probs;         // the rows are probabilities: p_j = value / Z
     float mt, md;
     double izt, izd;
     float inv_t;
@@ -548,6 +561,7 @@ struct SampleRows {
         izt = 1.0 / st.zt;
         inv_t = p.inv_t;
         V = p.V;
+        probs = p.probs != 0;
         residual = n < len;
         pd = pt;
         md = 0.0f;
@@ -560,7 +574,7 @@ struct SampleRows {
     }
 
     // visit(j, p_j, r_j) for j < cnt in order: p_j = exp((l - M) / T) / Z
-    // (fp32 exp, fp64 after); after a rejection r_j = max(0, p_j - q_j),
+    // (fp32 exp, fp64 after), or value / Z for probabilities; after a rejection r_j = max(0, p_j - q_j),
     // with no draft row r_j = 0.  Both rows are loaded before either is used.
     template <int kN, bool kVec, typename F>
     __device__ __forceinline__ void visit(int v0, int cnt, F &&f) const
@@ -574,10 +588,13 @@ struct SampleRows {
 #pragma unroll
         for (int j = 0; j < kN; ++j) {
             if (j < cnt) {
-                const double a = static_cast<double>(exp_cz((ft[j] - mt) * inv_t)) * izt;
+                const double a = probs ? static_cast<double>(ft[j]) * izt
+                                       : static_cast<double>(exp_cz((ft[j] - mt) * inv_t)) * izt;
                 double r = 0.0;
                 if (residual) {
-                    const double d = a - static_cast<double>(exp_cz((fd[j] - md) * inv_t)) * izd;
+                    const double b = probs ? static_cast<double>(fd[j]) * izd
+                                           : static_cast<double>(exp_cz((fd[j] - md) * inv_t)) * izd;
+                    const double d = a - b;
                     r = d > 0.0 ? d : 0.0;
                 }
                 f(j, a, r);
@@ -812,7 +829,9 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
 {
     const int64_t items = static_cast<int64_t>(p.B) * (2 * p.K + 1) * p.segs;
     const dim3 g1(static_cast<unsigned>((items + kWaves - 1) / kWaves));
-    if (sizeof(E) == 2 && p.split_ok)
+    if (sizeof(E) == 4 && p.probs)
+        hipLaunchKernelGGL((k_rej_stats<E, kProbs>), g1, dim3(kThreads), 0, s, p);
+    else if (sizeof(E) == 2 && p.split_ok)
         hipLaunchKernelGGL((k_rej_stats<E, kExpSplit>), g1, dim3(kThreads), 0, s, p);
     else if (p.inv_t == 1.0f)
         hipLaunchKernelGGL((k_rej_stats<E, kExpUnitT>), g1, dim3(kThreads), 0, s, p);

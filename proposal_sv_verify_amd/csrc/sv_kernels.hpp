@@ -112,6 +112,9 @@ struct RejectParams {
     float split_c1;
     float split_k2;
     int32_t split_ok;
+    // the rows are fp32 probabilities (a row's distribution is the row over
+    // its sum; no temperature) instead of logits
+    int32_t probs;
     // vocabulary shards: V above is the shard's width and the logit pointers
     // address its columns; v_offset is its first global id.  capture_x: the
     // statistics kernel records each row's logit at its draft token.

@@ -298,3 +298,20 @@ def test_suffix_rejects_bad_arguments(lib):
     assert lib.sv_last_error_message()
     assert lib.sv_suffix_workspace_bytes(0, 64, 0) == 0
     assert lib.sv_suffix_workspace_bytes(64, 8192, 262144) > 64 * 17 * 1024
+
+
+def test_rejection_probs_rejects_bad_arguments(lib):
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, rs=128, draft=FAKE, dl=None, u=FAKE, B=2, K=3, V=100, acc=FAKE,
+                 emi=FAKE, ws=FAKE, wsb=BIG)
+        a.update(kw)
+        return lib.sv_verify_rejection_probs(a["t"], a["d"], a["rs"], a["draft"], a["dl"], a["u"],
+                                             a["B"], a["K"], a["V"], a["acc"], a["emi"], None, None,
+                                             None, None, a["ws"], a["wsb"], None)
+    assert call(B=0) == sv.SV_ERR_INVALID_ARG
+    assert call(rs=99) == sv.SV_ERR_INVALID_ARG
+    assert call(draft=None) == sv.SV_ERR_INVALID_ARG
+    assert call(u=None) == sv.SV_ERR_INVALID_ARG
+    assert call(emi=None) == sv.SV_ERR_INVALID_ARG
+    assert call(wsb=8) == sv.SV_ERR_WORKSPACE
+    assert lib.sv_last_error_message()
