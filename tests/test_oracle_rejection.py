@@ -225,7 +225,7 @@ def test_masked_entries_equal_smaller_vocabulary(orc):
 
 @pytest.mark.parametrize("K", [1, 3])
 def test_probability_input_chisquare_v8(orc, K):
-    """With the target and draft given as probabilities (the north-star
+    """With the target and draft given as probabilities (the verifier's
     interface takes logits or probabilities), the emitted token at each
     reached position is distributed as p and the accept frequency is
     sum_x min(p, q); rows need not be normalised (the row's sum divides)."""
