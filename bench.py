@@ -337,6 +337,30 @@ def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
                 sample="%d full step(s): all four calls over every sequence (%.1f s)" % (n, el)), parity
 
 
+def stream_ceiling(reps=10):
+    """The measured streaming-read rate of this GPU: sv_read_probe (the
+    verifiers' 16-byte loads, nothing else) over 2 GiB, well above the
+    256 MiB last-level cache; HIP-event mean over reps after a warm-up."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    dev = torch.device("cuda:0")
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    call = sv.prepare_read_probe(buf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    call()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return dict(read_gb_per_s=round(gbs, 1), bytes=nbytes, kernel="sv_read_probe")
+
+
 def calibrate_copy():
     """A plain device copy of 256 MiB (reads 256 MiB, writes 256 MiB), three
     times: the reference launch for scaling FETCH_SIZE / WRITE_SIZE."""
@@ -374,6 +398,8 @@ def main():
                     help="skip the 16384-context n-gram measurement")
     ap.add_argument("--no-shards", action="store_true",
                     help="skip the vocabulary-sharded greedy and rejection measurements")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured copy / read ceiling")
     ap.add_argument("--no-suffix", action="store_true",
                     help="skip the suffix-decoding proposer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -429,6 +455,12 @@ def main():
                                        "bf16 alpha0.6; tree B32 N64 V128256 bf16",
                               positions_per_step=positions, proposals_per_step=64),
                   roofline=roofline, kernels=kernels)
+    if not args.no_ceiling:
+        ceil = stream_ceiling()
+        result["stream_ceiling"] = ceil
+        for k in kernels.values():
+            k["frac_of_measured_ceiling"] = round(k["gb_per_s"] / ceil["read_gb_per_s"], 4)
+        roofline["frac_of_measured_ceiling"] = round(achieved / ceil["read_gb_per_s"], 4)
     if not args.no_bandwidth_mode:
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
     if not args.no_suffix:

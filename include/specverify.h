@@ -370,6 +370,16 @@ int sv_rejection_shard_sample(const void *target_logits, const void *draft_logit
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sv_read_probe -- a measurement helper, not a step of the method: one
+ * streaming read of buf[0 .. bytes) with the verifiers' 16-byte loads, the
+ * reference their HBM rates are compared with.  buf: device memory,
+ * 16-byte aligned, bytes a positive multiple of 16; out: one device uint32
+ * (written only in a case that practically never occurs).  Enqueues one
+ * kernel on stream.
+ */
+int sv_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream);
+
+/*
  * Adaptive speculation length -- [Handbook] "adaptive" (the mechanism it
  * describes for SGLang): after each verification round, the mean number of
  * accepted draft tokens per sequence updates an exponential moving average,

@@ -40,7 +40,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_se
            "sv_rejection_shard_workspace_bytes", "sv_rejection_shard_stats",
            "sv_verify_rejection_partials", "sv_rejection_shard_mass", "sv_rejection_shard_sample",
            "sv_suffix_workspace_bytes", "sv_suffix_propose",
-           "sv_adaptive_init", "sv_adaptive_update")
+           "sv_read_probe", "sv_adaptive_init", "sv_adaptive_update")
 
 # One sv_argmax_partial: the row's largest value and the lowest global token
 # id holding it (NO_INDEX when the shard's row is all -inf).  The binding
@@ -131,6 +131,8 @@ def load(path: str = LIB_PATH):
         L.sv_suffix_propose.restype = ctypes.c_int
         L.sv_suffix_propose.argtypes = [P, i64, P, i32, P, i64, i32, i32, i32, ctypes.c_double,
                                         P, P, P, P, P, P, P, sz, P]
+        L.sv_read_probe.restype = ctypes.c_int
+        L.sv_read_probe.argtypes = [P, sz, P, P]
         L.sv_adaptive_init.restype = ctypes.c_int
         L.sv_adaptive_init.argtypes = [P, P, i32, ctypes.c_double, ctypes.c_double]
         L.sv_adaptive_update.restype = ctypes.c_int
@@ -700,6 +702,19 @@ def prepare_rejection_shard_sample(target, draft_logits, draft, uniforms, state,
 
 def rejection_shard_sample(*a, **k):
     return prepare_rejection_shard_sample(*a, **k)()
+
+
+# ---------------------------------------------------------------- measurement
+
+def prepare_read_probe(buf):
+    """One streaming read of a device tensor (16-byte aligned, a multiple
+    of 16 bytes) with the verifiers' loads: the reference rate."""
+    torch = _torch()
+    L = load()
+    out = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    args = (buf.data_ptr(), nbytes, out.data_ptr(), _stream(buf.device))
+    return Prepared(L.sv_read_probe, args, dict(out=out), (buf, out))
 
 
 # ---------------------------------------------------------------- adaptive length

@@ -924,6 +924,26 @@ int sv_rejection_shard_sample(const void *target_logits, const void *draft_logit
     return SV_OK;
 }
 
+// ------------------------------------------------------------------ probe
+
+int sv_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream)
+{
+    int st;
+    if (!buf || !out)
+        return fail(SV_ERR_INVALID_ARG, "buf and out are required");
+    if (bytes < 16 || bytes % 16 != 0 || misaligned(buf, 16))
+        return fail(SV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
+    if (bytes / 4 > (static_cast<size_t>(1) << 30) * static_cast<size_t>(g_target_wgs))
+        return fail(SV_ERR_UNSUPPORTED, "bytes too large");
+    if ((st = check_device()) != SV_OK)
+        return st;
+    hipError_t e = sv::launch_read_probe(buf, static_cast<int64_t>(bytes), out, g_target_wgs,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "probe launch");
+    return SV_OK;
+}
+
 // ------------------------------------------------------------------ suffix
 
 namespace {

@@ -206,4 +206,7 @@ struct SuffixParams {
 
 hipError_t launch_suffix(const SuffixParams &p, hipStream_t s);
 
+// a plain streaming read of `bytes` over about `wgs` workgroups
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int wgs, hipStream_t s);
+
 } // namespace sv

@@ -315,3 +315,11 @@ def test_rejection_probs_rejects_bad_arguments(lib):
     assert call(emi=None) == sv.SV_ERR_INVALID_ARG
     assert call(wsb=8) == sv.SV_ERR_WORKSPACE
     assert lib.sv_last_error_message()
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    assert lib.sv_read_probe(None, 1024, FAKE, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe(FAKE, 1024, None, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe(FAKE, 1000, FAKE, None) == sv.SV_ERR_INVALID_ARG   # not a multiple of 16
+    assert lib.sv_read_probe(FAKE + 4, 1024, FAKE, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_read_probe(FAKE, 0, FAKE, None) == sv.SV_ERR_INVALID_ARG
