@@ -274,11 +274,22 @@ def greedy_shards(gr, shards=8, reps=30):
                 gb_per_s_shard_calls=round(nbytes / t_shards / 1e3, 1), same_result=bool(same))
 
 
-def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs, step_bytes):
     """The oracle, as it stands, on the host cores: whole steps (all four
     calls, every sequence), sequences spread over a thread pool, for at
-    least `seconds` of wall time.  Also reports whether it agrees with the
-    GPU step's outputs."""
+    least `seconds` of wall time, then one step on a single thread.  Also
+    reports whether it agrees with the GPU step's outputs."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -318,6 +329,11 @@ def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
             break
     el = time.perf_counter() - t0
     pool.shutdown()
+    pool = ThreadPoolExecutor(1)
+    t1 = time.perf_counter()
+    step()
+    el1 = time.perf_counter() - t1
+    pool.shutdown()
     parity = None
     if gpu_outs is not None:
         g = gpu_outs
@@ -333,8 +349,11 @@ def cpu_baseline(ng, rj, gr, tr, seconds, gpu_outs):
         parity = dict(all_match=bool(ok), rejection_flagged_ties=int(tie.sum()),
                       rejection_mismatches=int((~same).sum()))
     return dict(value=round(4736 * n / el, 1), unit="verified positions/s", cores=threads,
-                kind="oracle",
-                sample="%d full step(s): all four calls over every sequence (%.1f s)" % (n, el)), parity
+                kind="oracle", cpu_model=cpu_model(),
+                gb_per_s=round(step_bytes * n / el / 1e9, 2),
+                value_1thread=round(4736 / el1, 1),
+                sample="%d full step(s): all four calls over every sequence (%.1f s); "
+                       "then one step on one thread (%.1f s)" % (n, el, el1)), parity
 
 
 def stream_ceiling(reps=10):
@@ -469,7 +488,8 @@ def main():
         result["greedy_vocab_shards"] = greedy_shards(gr)
         result["rejection_vocab_shards"] = rejection_shards(dev_inputs)
     if not args.no_cpu:
-        cb, parity = cpu_baseline(ng, rj, gr, tr, args.cpu_seconds, outs)
+        cb, parity = cpu_baseline(ng, rj, gr, tr, args.cpu_seconds, outs,
+                                  algo["rejection"] + algo["greedy"] + algo["tree"] + algo["ngram"])
         result["cpu_baseline"] = cb
         result["parity"] = parity
     print(json.dumps(result), flush=True)
