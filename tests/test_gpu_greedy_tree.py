@@ -111,6 +111,42 @@ def test_greedy_full_size_three_alphas(orc):
         assert abs(r["accepted"].mean() + 1 - tau) < 0.6
 
 
+def _plant_ties(logits, dtype, rng, frac=0.5):
+    """Copy each chosen row's maximum to 3 more random ids (lowest id wins)."""
+    B, R, V = logits.shape
+    wide = W.bf16_bits_to_f32(logits) if dtype == "bf16" else logits
+    for b in range(B):
+        for i in range(R):
+            if rng.random() < frac:
+                j = rng.choice(V, size=3, replace=False)
+                logits[b, i, j] = logits[b, i, np.argmax(wide[b, i])]
+
+
+@pytest.mark.parametrize("B,K,V,dtype", [
+    (256, 8, 32000, "bf16"),
+    (512, 3, 4096, "bf16"),
+    (256, 15, 8200, "f32"),
+    (256, 0, 5000, "f32"),       # the bonus row alone
+    (256, 6, 800, "bf16"),       # short rows, many of them
+    (256, 16, 4096, "bf16"),
+    (256, 8, 32001, "bf16"),     # V not a whole number of 16-byte vectors
+    (240, 8, 32000, "bf16"),
+])
+def test_greedy_large_batches(orc, B, K, V, dtype):
+    """Batches of 240-512 sequences, bit-exact: planted ties between ids far
+    apart in a row, the statistics counters and the out-of-range draft
+    flag."""
+    rng = np.random.default_rng(B + K + V)
+    wl = W.greedy_workload(B, K, V, dtype, 2.0, (0.6,), seed=B * 1000 + K)
+    logits = wl["logits"]
+    _plant_ties(logits, dtype, rng)
+    top = np.argmax(W.bf16_bits_to_f32(logits) if dtype == "bf16" else logits, axis=-1)[:, :K]
+    draft = W.planted_acceptance_drafts(top, V, 0.7, seed=K)
+    if K > 0:
+        draft[3, 0] = -2                  # flagged, never matches
+    _greedy_case(orc, logits, draft, label="B%d K%d V%d %s" % (B, K, V, dtype))
+
+
 def test_greedy_repeat_is_bit_identical(orc):
     """Same inputs, same (reused) workspace: identical outputs every time."""
     wl = W.greedy_workload(64, 8, 50000, "bf16", 2.0, (0.6,), seed=9)
