@@ -200,6 +200,57 @@ def suffix_proposer(reps=30):
                 from_history=int((out["source"] == 1).sum()))
 
 
+def greedy_small(reps=200):
+    """The small greedy workload (B 4, K 4, V 32000, fp32 logits N(0, 1),
+    planted acceptance 0.7): 20 rows, 2.56 MB, so the call is bound by
+    launch and memory latency, not bandwidth.  HIP-event mean per call."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    from proposal_sv_verify_amd import workloads as W
+
+    c = W.GREEDY_SMALL
+    wl = W.greedy_workload(c["B"], c["K"], c["V"], c["dtype"], c["sigma"], c["alphas"],
+                           seed=W.seed_for(1))
+    dev = torch.device("cuda:0")
+    call = sv.prepare_greedy(torch.from_numpy(wl["logits"]).to(dev),
+                             torch.from_numpy(wl["drafts"][c["alphas"][0]]).to(dev))
+    us = _timed([call], reps)
+    positions = c["B"] * (c["K"] + 1)
+    nbytes = positions * c["V"] * 4
+    return dict(B=c["B"], K=c["K"], V=c["V"], dtype=c["dtype"], us_per_call=round(us, 2),
+                positions_per_s=round(positions / us * 1e6, 1), algorithmic_bytes=nbytes,
+                gb_per_s=round(nbytes / us / 1e3, 1))
+
+
+def greedy_alphas(gr, reps=30):
+    """The large greedy workload's three planted acceptance rates on the same
+    logits (drafts planted from the numpy argmax of each row): HIP-event mean
+    per call, and the measured tokens per step beside the closed form
+    (1 - a^(K+1)) / (1 - a).  The call reads every row whatever the drafts,
+    so its time does not depend on the rate."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    from proposal_sv_verify_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    lg_np = gr["logits"]
+    B, K1, V = lg_np.shape
+    K = K1 - 1
+    top = W._row_argmax(lg_np[:, :K, :]).reshape(B, K)
+    lg = torch.from_numpy(lg_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    res = {}
+    for a in (0.3, 0.6, 0.9):
+        dr = W.planted_acceptance_drafts(top, V, a, seed=W.seed_for(4, salt=int(a * 10)))
+        call = sv.prepare_greedy(lg, torch.from_numpy(dr.astype(np.int32)).to(dev))
+        us = _timed([call], reps)
+        acc = call()["accepted"].cpu().numpy()
+        res["alpha_%.1f" % a] = dict(us_per_call=round(us, 2),
+                                     gb_per_s=round(B * K1 * V * 2 / us / 1e3, 1),
+                                     tokens_per_step=round(float(acc.mean()) + 1.0, 4),
+                                     tokens_per_step_closed_form=round((1 - a ** K1) / (1 - a), 4))
+    return res
+
+
 def rejection_shards(d, shards=8, reps=30):
     """The rejection workload in the eight 16032-column vocabulary shards
     of an 8-way tensor-parallel output layer: per-shard statistics, the
@@ -421,6 +472,8 @@ def main():
                     help="skip the measured copy / read ceiling")
     ap.add_argument("--no-suffix", action="store_true",
                     help="skip the suffix-decoding proposer measurement")
+    ap.add_argument("--no-greedy-extra", action="store_true",
+                    help="skip the small greedy workload and the acceptance-rate sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy a 256 MiB device buffer three times (a "
                          "kernel of known traffic for scaling the rocprofv3 byte counters)")
@@ -484,6 +537,9 @@ def main():
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
     if not args.no_suffix:
         result["suffix_proposer"] = suffix_proposer()
+    if not args.no_greedy_extra:
+        result["greedy_small"] = greedy_small()
+        result["greedy_alphas"] = greedy_alphas(gr)
     if not args.no_shards:
         result["greedy_vocab_shards"] = greedy_shards(gr)
         result["rejection_vocab_shards"] = rejection_shards(dev_inputs)
