@@ -4,8 +4,13 @@
  *
  *   sv_verify_greedy     greedy verification of K drafts per sequence
  *   sv_verify_rejection  rejection-sampling verification (target p, draft q)
+ *   sv_verify_rejection_probs  the same on given probabilities
  *   sv_verify_tree       greedy verification of a candidate tree
  *   sv_ngram_propose     n-gram prompt-lookup drafting
+ *   sv_suffix_propose    suffix-decoding drafting (context + shared history)
+ *   sv_argmax_shard, sv_verify_*_partials, sv_rejection_shard_*
+ *                        the verifiers on vocabulary-sharded logits
+ *   sv_adaptive_*        adaptive speculation length (host side)
  *
  * Pages this follows (section names as the pages give them):
  *  [Arctic]   "Fastest Speculative Decoding in vLLM with Arctic Inference and
