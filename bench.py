@@ -251,6 +251,83 @@ def greedy_alphas(gr, reps=30):
     return res
 
 
+def graph_steps(d, reps=100):
+    """The step's four calls captured once in a HIP graph and replayed,
+    beside the same calls launched one by one on the same stream; and a
+    small-batch decode step (n-gram proposals for 4 contexts of 2048 tokens,
+    then greedy verification of B 4, K 4, V 32000 fp32) where launching
+    dominates.  HIP-event means per step with the host running ahead, and
+    the host-observed median per step when the host waits for each step
+    (launch, then synchronise), as a decode loop does."""
+    import torch
+    import proposal_sv_verify_amd as sv
+    from proposal_sv_verify_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    s = torch.cuda.Stream(device=dev)
+
+    def measure(make):
+        with torch.cuda.stream(s):
+            calls = make()
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            eager = _timed(calls, reps)
+            graph = _timed([g.replay], reps)
+
+        def waited(fns):
+            # host-observed latency: launch, then wait for the stream, per step
+            for f in fns:
+                f()
+            s.synchronize()
+            t = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                for f in fns:
+                    f()
+                s.synchronize()
+                t.append(time.perf_counter() - t0)
+            return float(np.median(t)) * 1e6
+
+        with torch.cuda.stream(s):
+            eager_w = waited(calls)
+            graph_w = waited([g.replay])
+        return eager, graph, eager_w, graph_w
+
+    def main_step():
+        return [sv.prepare_ngram(d["ng_tok"], d["ng_len"], 2, 5, 8),
+                sv.prepare_rejection(d["rj_t"], d["rj_d"], d["rj_x"], d["rj_u"], 1.0),
+                sv.prepare_greedy(d["gr_l"], d["gr_x"]),
+                sv.prepare_tree(d["tr_l"], d["tr_p"], d["tr_t"])]
+
+    ng = W.ngram_workload(4, 2048, seed=W.seed_for(2, salt=3))
+    c1 = W.GREEDY_SMALL
+    g1 = W.greedy_workload(c1["B"], c1["K"], c1["V"], c1["dtype"], c1["sigma"], c1["alphas"],
+                           seed=W.seed_for(1))
+    small_in = [torch.from_numpy(a).to(dev) for a in
+                (ng["tokens"], ng["lengths"], g1["logits"], g1["drafts"][c1["alphas"][0]])]
+
+    def small_step():
+        return [sv.prepare_ngram(small_in[0], small_in[1], 2, 5, 8),
+                sv.prepare_greedy(small_in[2], small_in[3])]
+
+    e_main, g_main, ew_main, gw_main = measure(main_step)
+    e_small, g_small, ew_small, gw_small = measure(small_step)
+    positions = 64 * 6 + 256 * 9 + 32 * 64
+    return dict(step_us_eager=round(e_main, 2), step_us_graph=round(g_main, 2),
+                positions_per_s_graph=round(positions / g_main * 1e6, 1),
+                step_us_eager_waited=round(ew_main, 1), step_us_graph_waited=round(gw_main, 1),
+                small_step=dict(workload="ngram B4 L2048 + greedy B4 K4 V32000 f32",
+                                us_eager=round(e_small, 2), us_graph=round(g_small, 2),
+                                us_eager_waited=round(ew_small, 1), us_graph_waited=round(gw_small, 1)))
+
+
 def rejection_shards(d, shards=8, reps=30):
     """The rejection workload in the eight 16032-column vocabulary shards
     of an 8-way tensor-parallel output layer: per-shard statistics, the
@@ -472,6 +549,8 @@ def main():
                     help="skip the measured copy / read ceiling")
     ap.add_argument("--no-suffix", action="store_true",
                     help="skip the suffix-decoding proposer measurement")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step and of a small-batch step")
     ap.add_argument("--no-greedy-extra", action="store_true",
                     help="skip the small greedy workload and the acceptance-rate sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -537,6 +616,8 @@ def main():
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
     if not args.no_suffix:
         result["suffix_proposer"] = suffix_proposer()
+    if not args.no_graph:
+        result["graph_step"] = graph_steps(dev_inputs)
     if not args.no_greedy_extra:
         result["greedy_small"] = greedy_small()
         result["greedy_alphas"] = greedy_alphas(gr)
