@@ -364,7 +364,7 @@ constexpr int kRound = 64 * kHdr;     // chunks per gather round
 // Per-wave LDS of the path kernel.
 struct PathLds {
     int occ[kOcc];                    // end positions, most recent first
-    int tok[kOcc];                    // this depth's next token per occurrence
+    int tok[kOcc];                    // this depth's continuing tokens, packed
     int end[kRound];                  // gather: inclusive end of each chunk's slots
     int cont[SV_SUFFIX_MAX_K][kOcc];  // continuation tokens [depth][occurrence]
     int path[SV_SUFFIX_MAX_K];
@@ -503,11 +503,21 @@ __device__ void text_path(const SuffixParams &p, int b, bool hist, PathLds &W)
                 count = nv;
                 x = x0;
             } else {
+                // the continuing occurrences' tokens packed into W.tok[0, nv)
+                // (their order does not matter), so that one pass over them
+                // counts all of a lane's tokens; occurrences off the path do
+                // not take part, and the path narrows them step by step
+                int base = 0;
 #pragma unroll
-                for (int q = 0; q < kPer; ++q)
-                    W.tok[lane + 64 * q] = tok[q];
+                for (int q = 0; q < kPer; ++q) {
+                    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(val[q] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(val[q]), 0));
+                    if (tok[q] >= 0)
+                        W.tok[base + below] = tok[q];
+                    base += __popcll(val[q]);
+                }
                 int mc[kPer] = {};
-                for (int k = 0; k < n; ++k) {            // one pass counts all of a lane's tokens
+                for (int k = 0; k < nv; ++k) {           // one pass counts all of a lane's tokens
                     const int y = W.tok[k];
 #pragma unroll
                     for (int q = 0; q < kPer; ++q)
