@@ -1,0 +1,157 @@
+"""GPU parity on seeded random mixes of the parameters the other tests vary
+one at a time: shapes, dtypes, row strides padded past V, base pointers a
+few elements into their allocation, draft lengths, out-of-range ids,
+temperatures, masked vocabularies, malformed trees, bad context lengths.
+Each case is checked against the oracle: bit-exact for greedy, tree and
+n-gram; decisions equal except oracle-flagged ties for rejection sampling
+(logits and probabilities)."""
+import numpy as np
+import pytest
+import torch
+
+import proposal_sv_verify_amd as sv
+from proposal_sv_verify_amd import workloads as W
+from gpu_util import check_rejection, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = 60
+
+
+def _view(a, pad, off):
+    """a [..., V] on the device with row stride V + pad, its first element
+    `off` elements into the allocation."""
+    V = a.shape[-1]
+    rows = int(np.prod(a.shape[:-1]))
+    stride = V + pad
+    flat = np.zeros(rows * stride + off + 8, a.dtype)
+    flat[off:off + rows * stride].reshape(rows, stride)[:, :V] = a.reshape(rows, V)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(flat.view(np.int16)).to(dev()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(flat).to(dev())
+    return t[off:off + rows * stride].view(*a.shape[:-1], stride)[..., :V]
+
+
+def _dv(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def _same(g, r, keys, label):
+    for k in keys:
+        np.testing.assert_array_equal(host(g[k]).astype(np.int64), np.asarray(r[k]).astype(np.int64),
+                                      err_msg="%s %s" % (label, k))
+
+
+def test_random_greedy(orc):
+    rng = np.random.default_rng(101)
+    for i in range(CASES):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        B, K = int(rng.integers(1, 13)), int(rng.integers(0, 10))
+        V = int(rng.choice([1, 2, 3, 7, 8, 13, 100, 1000, 4099, 20000, 65539]))
+        wl = W.greedy_workload(B, K, V, dtype, 2.0, (0.6,), seed=1000 + i)
+        lg = wl["logits"]
+        if V > 4 and rng.random() < 0.5:              # duplicate the maximum in one row
+            wide = W.bf16_bits_to_f32(lg) if dtype == "bf16" else lg
+            b, r = int(rng.integers(0, B)), int(rng.integers(0, K + 1))
+            lg[b, r, rng.choice(V, size=3, replace=False)] = lg[b, r, np.argmax(wide[b, r])]
+        draft = wl["drafts"][0.6].copy()
+        if K > 0 and rng.random() < 0.2:
+            draft[0, 0] = V + 4
+        dl = rng.integers(-1, K + 2, size=B).astype(np.int32) if rng.random() < 0.4 else None
+        pad, off = int(rng.choice([0, 1, 5, 64])), int(rng.choice([0, 1, 3]))
+        label = "greedy %d %s B%d K%d V%d pad%d off%d" % (i, dtype, B, K, V, pad, off)
+        say(label)
+        g = sv.verify_greedy(_view(lg, pad, off), _dv(draft), _dv(dl) if dl is not None else None)
+        _same(g, orc.verify_greedy(lg, draft, dl), ("accepted", "emitted", "argmax", "flags"), label)
+
+
+def test_random_tree(orc):
+    rng = np.random.default_rng(102)
+    for i in range(CASES):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        B, N = int(rng.integers(1, 9)), int(rng.integers(1, 70))
+        V = int(rng.choice([9, 12, 64, 777, 3001, 40000]))
+        wl = W.tree_workload(B, N, V, 2.0, 0.8, N, int(rng.choice([2, 4, 8])), seed=2000 + i, dtype=dtype)
+        parent, token = wl["parent"].copy(), wl["token"].copy()
+        if N > 3 and rng.random() < 0.3:
+            parent[0, N - 1] = N + 2
+            token[0, 1] = -3
+        pad, off = int(rng.choice([0, 1, 7])), int(rng.choice([0, 2]))
+        label = "tree %d %s B%d N%d V%d pad%d off%d" % (i, dtype, B, N, V, pad, off)
+        say(label)
+        g = sv.verify_tree(_view(wl["logits"], pad, off), _dv(parent), _dv(token))
+        _same(g, orc.verify_tree(wl["logits"], parent, token),
+              ("accepted", "path", "emitted", "argmax", "flags"), label)
+
+
+def test_random_rejection(orc):
+    rng = np.random.default_rng(103)
+    total_flag = total_mism = 0
+    for i in range(CASES):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        B, K = int(rng.integers(1, 13)), int(rng.integers(0, 8))
+        V = int(rng.choice([1, 2, 8, 9, 100, 1000, 4097, 9000, 30000, 70001]))
+        T = float(rng.choice([0.4, 1.0, 1.9]))
+        top_k = int(rng.choice([0, 0, 1, 5, 50])) if V > 50 else 0
+        wl = W.rejection_workload(B, K, V, 2.0, 0.7, T, seed=3000 + i, dtype=dtype, top_k=top_k or None)
+        draft = wl["draft"].copy()
+        if K > 0 and rng.random() < 0.2:
+            draft[0, 0] = V + 3
+        dl = rng.integers(-1, K + 2, size=B).astype(np.int32) if rng.random() < 0.4 else None
+        pad, off = int(rng.choice([0, 1, 8])), int(rng.choice([0, 1]))
+        label = "rejection %d %s B%d K%d V%d T%.1f top%d pad%d off%d" % (i, dtype, B, K, V, T, top_k, pad, off)
+        say(label)
+        tg = _view(wl["target"], pad, off)
+        dg = _view(wl["draft_logits"], pad, off) if K > 0 else None
+        g = sv.verify_rejection(tg, dg, _dv(draft), _dv(wl["uniforms"]), T,
+                                _dv(dl) if dl is not None else None)
+        r = orc.verify_rejection(wl["target"], wl["draft_logits"], draft, wl["uniforms"], T, dl)
+        f, m = check_rejection(g, r, label)
+        _same(g, r, ("flags",), label)
+        total_flag += f
+        total_mism += m
+    assert total_mism <= total_flag
+
+
+def test_random_rejection_probs(orc):
+    rng = np.random.default_rng(104)
+    for i in range(CASES):
+        B, K = int(rng.integers(1, 10)), int(rng.integers(0, 6))
+        V = int(rng.choice([1, 3, 8, 64, 1001, 5000]))
+        P = rng.dirichlet(np.full(V, 0.3), size=(B, K + 1)).astype(np.float32)
+        Q = rng.dirichlet(np.full(V, 0.3), size=(B, K)).astype(np.float32)
+        P[P < 1e-4] = 0.0                             # zero entries, rows not normalised
+        P[..., 0] += 1e-3
+        Q[Q < 1e-4] = 0.0
+        if K > 0:
+            Q[..., -1] += 1e-3
+        P *= np.float32(rng.uniform(0.5, 3.0))
+        draft = np.array([[rng.choice(V, p=Q[b, k] / Q[b, k].sum()) for k in range(K)] for b in range(B)],
+                         np.int32).reshape(B, K)
+        u = rng.random((B, K + 1), dtype=np.float32)
+        pad, off = int(rng.choice([0, 1, 4])), int(rng.choice([0, 1]))
+        label = "probs %d B%d K%d V%d pad%d off%d" % (i, B, K, V, pad, off)
+        say(label)
+        g = sv.verify_rejection_probs(_view(P, pad, off), _view(Q, pad, off) if K > 0 else None,
+                                      _dv(draft), _dv(u))
+        f, m = check_rejection(g, orc.verify_rejection(P, Q, draft, u, 1.0, None, probs=True), label)
+        assert m <= f
+
+
+def test_random_ngram(orc):
+    rng = np.random.default_rng(105)
+    for i in range(CASES):
+        B = int(rng.integers(1, 40))
+        stride = int(rng.choice([1, 5, 31, 256, 1000, 4099]))
+        alpha = int(rng.choice([2, 3, 5, 50]))
+        tokens = rng.integers(0, alpha, (B, stride)).astype(np.int32)
+        lengths = rng.integers(-2, stride + 3, size=B).astype(np.int32)
+        n_min = int(rng.integers(1, 5))
+        n_max = int(rng.integers(n_min, 9))
+        K = int(rng.integers(0, 12))
+        label = "ngram %d B%d stride%d alphabet%d n%d-%d K%d" % (i, B, stride, alpha, n_min, n_max, K)
+        say(label)
+        g = sv.ngram_propose(_dv(tokens), _dv(lengths), n_min, n_max, K)
+        _same(g, orc.ngram_propose(tokens, lengths, n_min, n_max, K),
+              ("proposal", "proposal_len", "match_n", "match_pos", "flags"), label)
