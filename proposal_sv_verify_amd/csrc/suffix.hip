@@ -358,6 +358,7 @@ __device__ __forceinline__ long long wave_max_i64(long long x)
 }
 
 constexpr int kPer = kOcc / 64;       // occurrences per lane in the path wave
+constexpr int kSortMin = 64;          // above this many continuing occurrences a step sorts them
 constexpr int kHdr = 8;               // chunk headers per lane per gather round
 constexpr int kRound = 64 * kHdr;     // chunks per gather round
 
@@ -382,6 +383,68 @@ __device__ __forceinline__ int wave_inclusive_int(int x)
             x += y;
     }
     return x;
+}
+
+// The most frequent token among a wave's kOcc slots (kPer per lane; values
+// below 0 are empty), the lowest token on equal counts, as the key
+// (count << 32) | (0x7fffffff - token), 0 when every slot is empty: a
+// bitonic sort of the slots in element order 4 * lane + q (partners kPer or
+// more apart are in other lanes), then each run of equal values is measured
+// from its first element, found by a max-scan of the run heads.
+__device__ long long wave_mode(const int (&tok)[kPer])
+{
+    const int lane = threadIdx.x & 63;
+    int v[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+        v[q] = tok[q] >= 0 ? tok[q] : -1;
+#pragma unroll
+    for (int k = 2; k <= kPer * 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            int o[kPer];
+#pragma unroll
+            for (int q = 0; q < kPer; ++q)
+                o[q] = j >= kPer ? __shfl_xor(v[q], j / kPer, 64) : v[q ^ (j % kPer)];
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                const int i = kPer * lane + q;
+                const bool up = (i & k) == 0, low = (i & j) == 0;
+                v[q] = up == low ? min(v[q], o[q]) : max(v[q], o[q]);
+            }
+        }
+    }
+    // runs: start[q] = the index of the first element of element q's run
+    const int prev = __shfl_up(v[kPer - 1], 1, 64);
+    const int next = __shfl_down(v[0], 1, 64);
+    int start[kPer];
+    int s = -1;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int pv = q == 0 ? prev : v[q - 1];
+        if ((lane == 0 && q == 0) || v[q] != pv)
+            s = kPer * lane + q;
+        start[q] = s;
+    }
+    int scan = s;                                 // inclusive max-scan of the lanes' last heads
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(scan, off, 64);
+        if (lane >= off)
+            scan = max(scan, y);
+    }
+    const int before = __shfl_up(scan, 1, 64);    // the last head in earlier lanes
+    long long key = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = kPer * lane + q;
+        const int st = start[q] >= 0 ? start[q] : before;
+        const int nv = q + 1 < kPer ? v[q + 1] : next;
+        const bool end = (lane == 63 && q == kPer - 1) || v[q] != nv;
+        if (end && v[q] >= 0)
+            key = max(key, (static_cast<long long>(i - st + 1) << 32) | (0x7fffffffll - v[q]));
+    }
+    return wave_max_i64(key);
 }
 
 // The path of one text, computed by one wave (all control flow is uniform
@@ -502,6 +565,10 @@ __device__ void text_path(const SuffixParams &p, int b, bool hist, PathLds &W)
             if (!differ) {                         // every continuing occurrence agrees
                 count = nv;
                 x = x0;
+            } else if (nv > kSortMin) {
+                const long long key = wave_mode(tok);
+                count = static_cast<int>(key >> 32);
+                x = static_cast<int>(0x7fffffffll - (key & 0xffffffffll));
             } else {
                 // the continuing occurrences' tokens packed into W.tok[0, nv)
                 // (their order does not matter), so that one pass over them
