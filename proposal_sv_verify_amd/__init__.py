@@ -184,6 +184,25 @@ def workspace(nbytes: int, device, stream=None):
     return buf
 
 
+def _row_stride(x, rows_dims, name):
+    """Elements between consecutive rows of a [.., V] tensor whose first
+    rows_dims dims index evenly spaced rows, and whose last dim has unit
+    stride.  Dims of size 1 do not constrain it (torch leaves their stride
+    arbitrary); a single row gets V."""
+    if x.dim() != rows_dims + 1 or (x.size(-1) > 1 and x.stride(-1) != 1):
+        raise ValueError("%s must be [%s, V] with unit stride along V" % (name, "..." * rows_dims))
+    rs = None
+    span = 1                                      # rows one step of dim d moves over
+    for d in range(rows_dims - 1, -1, -1):
+        if x.size(d) > 1:
+            if rs is None:
+                rs = x.stride(d) // span if x.stride(d) % span == 0 else -1
+            if rs < 0 or x.stride(d) != rs * span:
+                raise ValueError("%s rows must be evenly spaced; call .contiguous()" % name)
+        span *= x.size(d)
+    return x.size(-1) if rs is None else rs
+
+
 def _logits_args(x, name, rows_dims):
     """Validate a [.., V] logits tensor whose leading dims are evenly spaced
     rows; returns (dtype code, row stride in elements)."""
@@ -196,13 +215,7 @@ def _logits_args(x, name, rows_dims):
         code = SV_F32
     else:
         raise TypeError("%s must be float32 or bfloat16, got %s" % (name, x.dtype))
-    if x.dim() != rows_dims + 1 or x.stride(-1) != 1:
-        raise ValueError("%s must be [%s, V] with unit stride along V" % (name, "..." * rows_dims))
-    rs = x.stride(-2)
-    for d in range(rows_dims - 1):
-        if x.stride(d) != x.size(d + 1) * x.stride(d + 1):
-            raise ValueError("%s rows must be evenly spaced; call .contiguous()" % name)
-    return code, rs
+    return code, _row_stride(x, rows_dims, name)
 
 
 def _rows_readable(t, rows, stride, name):
@@ -400,10 +413,10 @@ def prepare_ngram(tokens, lengths, n_min, n_max, K):
     match_n [B], match_pos [B], flags [B]."""
     torch = _torch()
     L = load()
-    if tokens.dtype != torch.int32 or tokens.dim() != 2 or tokens.stride(1) != 1:
+    if tokens.dtype != torch.int32:
         raise ValueError("tokens must be an int32 [B, stride] tensor with unit inner stride")
     B = tokens.shape[0]
-    stride = tokens.stride(0)
+    stride = _row_stride(tokens, 1, "tokens")
     dev = tokens.device
     _rows_readable(tokens, B, stride, "tokens")
     _i32(lengths, (B,), "lengths")
@@ -430,10 +443,10 @@ def prepare_suffix(tokens, lengths, history, m_min, m_max, K, min_prob):
     match_len [B], source [B] (0 context, 1 history, -1 none), flags [B]."""
     torch = _torch()
     L = load()
-    if tokens.dtype != torch.int32 or tokens.dim() != 2 or tokens.stride(1) != 1:
+    if tokens.dtype != torch.int32:
         raise ValueError("tokens must be an int32 [B, stride] tensor with unit inner stride")
     B = tokens.shape[0]
-    stride = tokens.stride(0)
+    stride = _row_stride(tokens, 1, "tokens")
     dev = tokens.device
     _rows_readable(tokens, B, stride, "tokens")
     _i32(lengths, (B,), "lengths")

@@ -89,3 +89,22 @@ def test_suffix_unaligned_views(orc):
     r = orc.suffix_propose(wl["tokens"], wl["lengths"], wl["history"], 1, 32, 12, 0.2)
     for k in ("proposal", "proposal_len", "match_len", "source", "score"):
         np.testing.assert_array_equal(host(g[k]), r[k], err_msg=k)
+
+
+@pytest.mark.parametrize("n7,n3,want", [(40, 40, 3), (41, 39, 7)])
+def test_suffix_counts_on_a_sorted_step(orc, n7, n3, want):
+    """More than 64 occurrences continue the first step (the step sorts
+    their tokens across the wave): the pattern is followed n7 times by
+    token 7 and n3 times by token 3 in the history.  Equal counts go to
+    the lower id; one more occurrence decides otherwise."""
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(1000, 2000, size=300).astype(np.int32)
+    ctx[-2:] = [500, 501]
+    docs = []
+    for t in rng.permutation([7] * n7 + [3] * n3):
+        docs += list(rng.integers(2000, 3000, size=int(rng.integers(3, 9)))) + [500, 501, int(t)]
+        docs += list(rng.integers(2000, 3000, size=3)) + [-1]
+    hist = np.array(docs, np.int32)
+    r = _case(orc, ctx[None, :], np.array([300], np.int32), hist, 1, 8, 4, 0.1,
+              "counts %d/%d" % (n7, n3))
+    assert r["source"][0] == 1 and r["proposal"][0, 0] == want
