@@ -184,11 +184,12 @@ def workspace(nbytes: int, device, stream=None):
     return buf
 
 
-def _row_stride(x, rows_dims, name):
+def _row_stride(x, rows_dims, name, single=None):
     """Elements between consecutive rows of a [.., V] tensor whose first
     rows_dims dims index evenly spaced rows, and whose last dim has unit
     stride.  Dims of size 1 do not constrain it (torch leaves their stride
-    arbitrary); a single row gets V."""
+    arbitrary); a single row takes `single` (the stride of a tensor it is
+    passed with), else V."""
     if x.dim() != rows_dims + 1 or (x.size(-1) > 1 and x.stride(-1) != 1):
         raise ValueError("%s must be [%s, V] with unit stride along V" % (name, "..." * rows_dims))
     rs = None
@@ -200,10 +201,12 @@ def _row_stride(x, rows_dims, name):
             if rs < 0 or x.stride(d) != rs * span:
                 raise ValueError("%s rows must be evenly spaced; call .contiguous()" % name)
         span *= x.size(d)
-    return x.size(-1) if rs is None else rs
+    if rs is None:
+        return x.size(-1) if single is None else single
+    return rs
 
 
-def _logits_args(x, name, rows_dims):
+def _logits_args(x, name, rows_dims, single=None):
     """Validate a [.., V] logits tensor whose leading dims are evenly spaced
     rows; returns (dtype code, row stride in elements)."""
     torch = _torch()
@@ -215,7 +218,7 @@ def _logits_args(x, name, rows_dims):
         code = SV_F32
     else:
         raise TypeError("%s must be float32 or bfloat16, got %s" % (name, x.dtype))
-    return code, _row_stride(x, rows_dims, name)
+    return code, _row_stride(x, rows_dims, name, single)
 
 
 def _rows_readable(t, rows, stride, name):
@@ -300,7 +303,7 @@ def prepare_rejection(target, draft_logits, draft, uniforms, temperature=1.0, dr
     K = K1 - 1
     dev = target.device
     if K > 0:
-        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2)
+        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2, single=rs)
         if code2 != code or rs2 != rs or tuple(draft_logits.shape) != (B, K, V):
             raise ValueError("draft_logits must be [B, K, V] with the target's dtype and row stride")
     _i32(draft, (B, K), "draft")
@@ -346,7 +349,7 @@ def prepare_rejection_probs(target_probs, draft_probs, draft, uniforms, draft_le
     K = K1 - 1
     dev = target_probs.device
     if K > 0:
-        _, rs2 = _logits_args(draft_probs, "draft_probs", 2)
+        _, rs2 = _logits_args(draft_probs, "draft_probs", 2, single=rs)
         if draft_probs.dtype != torch.float32 or rs2 != rs or tuple(draft_probs.shape) != (B, K, V):
             raise ValueError("draft_probs must be float32 [B, K, V] with the target's row stride")
     _i32(draft, (B, K), "draft")
@@ -577,7 +580,7 @@ def _shard_logits(target, draft_logits):
     B, K1, Vs = target.shape
     K = K1 - 1
     if K > 0:
-        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2)
+        code2, rs2 = _logits_args(draft_logits, "draft_logits", 2, single=rs)
         if code2 != code or rs2 != rs or tuple(draft_logits.shape) != (B, K, Vs):
             raise ValueError("draft_logits must be [B, K, Vs] with the target's dtype and row stride")
     return code, rs, B, K, Vs

@@ -43,3 +43,17 @@ def test_uneven_rows_and_inner_stride_are_rejected():
         _row_stride(y, 1, "y")
     with pytest.raises(ValueError):
         _row_stride(torch.zeros(4, 9), 2, "z")             # wrong rank
+
+
+def test_single_row_takes_the_partner_stride():
+    """A draft tensor of one row ([1, 1, V]) is passed with a target whose
+    rows are padded: its own stride is unconstrained, so it takes the
+    target's."""
+    big = torch.zeros(1, 3, 12)
+    target = big[:, :2, :7]                                # rows 12 apart
+    draft = big[:, 2:, :7]                                 # one row
+    assert _row_stride(target, 2, "t") == 12
+    assert _row_stride(draft, 2, "d") == 7
+    assert _row_stride(draft, 2, "d", single=12) == 12
+    two = torch.zeros(2, 1, 12)[..., :7]                   # two rows: the stride is fixed
+    assert _row_stride(two, 2, "d", single=99) == 12
