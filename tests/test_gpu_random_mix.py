@@ -155,3 +155,23 @@ def test_random_ngram(orc):
         g = sv.ngram_propose(_dv(tokens), _dv(lengths), n_min, n_max, K)
         _same(g, orc.ngram_propose(tokens, lengths, n_min, n_max, K),
               ("proposal", "proposal_len", "match_n", "match_pos", "flags"), label)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_row_draft_beside_padded_target(orc, dtype):
+    """B = 1, K = 1: the draft tensor is a single row, so its own stride is
+    unconstrained and the call uses the padded target's."""
+    wl = W.rejection_workload(1, 1, 3001, 2.0, 0.7, 1.0, seed=77, dtype=dtype)
+    tg, dg = _view(wl["target"], 5, 1), _view(wl["draft_logits"], 5, 1)
+    say("one-row draft", dtype, tuple(tg.shape), tg.stride(), tuple(dg.shape), dg.stride())
+    g = sv.verify_rejection(tg, dg, _dv(wl["draft"]), _dv(wl["uniforms"]), 1.0)
+    r = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], wl["uniforms"], 1.0)
+    f, m = check_rejection(g, r, "one-row draft " + dtype)
+    assert m <= f
+    if dtype == "f32":
+        P = np.exp(wl["target"] - wl["target"].max(-1, keepdims=True)).astype(np.float32)
+        Q = np.exp(wl["draft_logits"] - wl["draft_logits"].max(-1, keepdims=True)).astype(np.float32)
+        g = sv.verify_rejection_probs(_view(P, 5, 1), _view(Q, 5, 1), _dv(wl["draft"]), _dv(wl["uniforms"]))
+        r = orc.verify_rejection(P, Q, wl["draft"], wl["uniforms"], 1.0, None, probs=True)
+        f, m = check_rejection(g, r, "one-row draft probs")
+        assert m <= f
