@@ -175,3 +175,90 @@ def test_one_row_draft_beside_padded_target(orc, dtype):
         r = orc.verify_rejection(P, Q, wl["draft"], wl["uniforms"], 1.0, None, probs=True)
         f, m = check_rejection(g, r, "one-row draft probs")
         assert m <= f
+
+
+def _cuts(rng, V, P):
+    P = min(P, V)
+    inner = sorted(int(c) for c in rng.choice(np.arange(1, V), size=P - 1, replace=False)) if P > 1 else []
+    c = [0] + inner + [V]
+    return list(zip(c[:-1], c[1:]))
+
+
+def test_random_vocabulary_shards(orc):
+    """Greedy and rejection sampling over 1-8 vocabulary shards cut at random
+    columns of padded, offset rows: the shard calls' combined results equal
+    the oracle's on the whole rows."""
+    rng = np.random.default_rng(106)
+    for i in range(40):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        B, K = int(rng.integers(1, 9)), int(rng.integers(0, 6))
+        V = int(rng.choice([2, 9, 100, 3001, 20000]))
+        pad, off = int(rng.choice([0, 3])), int(rng.choice([0, 1]))
+        dl = rng.integers(-1, K + 2, size=B).astype(np.int32) if rng.random() < 0.4 else None
+        dlt = _dv(dl) if dl is not None else None
+        if i % 2 == 0:
+            wl = W.greedy_workload(B, K, V, dtype, 2.0, (0.6,), seed=5000 + i)
+            shards = _cuts(rng, V, int(rng.integers(1, 9)))
+            label = "shard greedy %d %s B%d K%d V%d P%d" % (i, dtype, B, K, V, len(shards))
+            say(label)
+            lg = _view(wl["logits"], pad, off)
+            parts = torch.empty(len(shards), B * (K + 1), dtype=torch.int64, device=dev())
+            for p, (a, b) in enumerate(shards):
+                sv.argmax_shard(lg[..., a:b], a, out=parts[p])
+            g = sv.verify_greedy_partials(parts, _dv(wl["drafts"][0.6]), V, dlt)
+            _same(g, orc.verify_greedy(wl["logits"], wl["drafts"][0.6], dl),
+                  ("accepted", "emitted", "argmax", "flags"), label)
+        else:
+            V = max(V, 9)
+            T = float(rng.choice([0.5, 1.0, 1.6]))
+            wl = W.rejection_workload(B, K, V, 2.0, 0.7, T, seed=6000 + i, dtype=dtype)
+            shards = _cuts(rng, V, int(rng.integers(1, 7)))
+            label = "shard rejection %d %s B%d K%d V%d P%d T%.1f" % (i, dtype, B, K, V, len(shards), T)
+            say(label)
+            tg = _view(wl["target"], pad, off)
+            dg = _view(wl["draft_logits"], pad, off) if K > 0 else None
+            dr, u = _dv(wl["draft"]), _dv(wl["uniforms"])
+            P = len(shards)
+            parts = torch.empty(P, B * (2 * K + 1), 2, dtype=torch.float64, device=dev())
+            for p, (a, b) in enumerate(shards):
+                sv.rejection_shard_stats(tg[..., a:b], dg[..., a:b] if K > 0 else None, dr, a, T, dlt,
+                                         out=parts[p])
+            dec = sv.verify_rejection_partials(parts, dr, u, V, T, dlt)
+            masses = torch.empty(P, B, 2, dtype=torch.float64, device=dev())
+            wss = []
+            for p, (a, b) in enumerate(shards):
+                m = sv.rejection_shard_mass(tg[..., a:b], dg[..., a:b] if K > 0 else None, dec["state"], T,
+                                            out=masses[p])
+                wss.append(m["workspace"])
+            emitted = torch.full((B, K + 1), -7, dtype=torch.int32, device=dev())
+            for p, (a, b) in enumerate(shards):
+                sv.rejection_shard_sample(tg[..., a:b], dg[..., a:b] if K > 0 else None, dr, u, dec["state"],
+                                          masses, p, a, wss[p], emitted, T)
+            out = dict(dec)
+            out["emitted"] = emitted
+            r = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], wl["uniforms"], T, dl)
+            f, m = check_rejection(out, r, label)
+            assert m <= f
+
+
+def test_random_suffix(orc):
+    rng = np.random.default_rng(107)
+    for i in range(40):
+        B = int(rng.integers(1, 20))
+        stride = int(rng.choice([3, 40, 333, 2048, 5003]))
+        alpha = int(rng.choice([2, 3, 6, 40]))
+        tokens = rng.integers(0, alpha, (B, stride)).astype(np.int32)
+        lengths = rng.integers(-1, stride + 2, size=B).astype(np.int32)
+        H = int(rng.choice([0, 1, 500, 20000]))
+        hist = rng.integers(-1, alpha, size=H).astype(np.int32) if H else None
+        m_min = int(rng.integers(1, 4))
+        m_max = int(rng.integers(m_min, 33))
+        K = int(rng.integers(0, 17))
+        mp = float(rng.choice([0.0, 0.1, 0.5, 1.0]))
+        label = "suffix %d B%d stride%d alphabet%d H%d m%d-%d K%d p%.1f" % (i, B, stride, alpha, H, m_min, m_max, K, mp)
+        say(label)
+        g = sv.suffix_propose(_dv(tokens), _dv(lengths), _dv(hist) if hist is not None else None,
+                              m_min, m_max, K, mp)
+        r = orc.suffix_propose(tokens, lengths, hist, m_min, m_max, K, mp)
+        _same(g, r, ("proposal", "proposal_len", "match_len", "source", "flags"), label)
+        np.testing.assert_array_equal(host(g["score"]), r["score"], err_msg=label + " score")
