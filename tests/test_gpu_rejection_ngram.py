@@ -40,6 +40,19 @@ def test_rejection_full_size(orc):
     assert mism <= flagged
 
 
+def test_rejection_full_size_more_seeds(orc):
+    """Four more seeds of the full-size workload (256 sequences): every
+    decision that differs from the oracle's lies in a flagged tie."""
+    total_flag = total_mism = 0
+    for salt in range(4):
+        wl = W.rejection_workload(**W.REJECTION, seed=W.seed_for(3, salt=100 + salt))
+        f, m = _rej_case(orc, wl, label="B64K5V128256 salt %d" % salt)
+        total_flag += f
+        total_mism += m
+    say("rejection full size, 4 seeds: flagged %d, mismatched %d of 256" % (total_flag, total_mism))
+    assert total_mism <= total_flag
+
+
 @pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
 def test_rejection_small_shapes_temperatures(orc, T):
     rng = np.random.default_rng(int(T * 10))
