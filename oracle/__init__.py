@@ -94,6 +94,8 @@ class Oracle:
         L.orc_verify_rejection.argtypes = [P, P, ctypes.c_int, i64, P, P, P, dbl, i32, i32, i32,
                                            dbl, dbl, P, P, P, P, P, P, P]
         L.orc_verify_rejection.restype = None
+        L.orc_sample_cdf.argtypes = [P, P, ctypes.c_int, i32, dbl, P]
+        L.orc_sample_cdf.restype = dbl
         L.orc_verify_tree.argtypes = [P, ctypes.c_int, i64, P, P, i32, i32, i32, P, P, P, P, P]
         L.orc_verify_tree.restype = None
         L.orc_ngram_propose.argtypes = [P, i64, P, i32, i32, i32, i32, P, P, P, P, P]
@@ -156,6 +158,24 @@ class Oracle:
                                       _ptr(st), _ptr(flg))
         return dict(accepted=acc, emitted=emi, p_draft=pd, q_draft=qd,
                     accept_tie=at.astype(bool), sample_tie=st.astype(bool), flags=flg)
+
+    def sample_cdf(self, target_row, draft_row=None, temperature=1.0, probs=False):
+        """The final sample's distribution for one row pair: returns (C, S)
+        with C[v] the cumulative mass of r = max(0, p - q) (or of p when
+        draft_row is None or the residual is empty) up to token v, S = C[-1]."""
+        target_row = np.ascontiguousarray(target_row)
+        V = target_row.shape[-1]
+        if draft_row is not None:
+            draft_row = np.ascontiguousarray(draft_row)
+            if draft_row.shape != target_row.shape or draft_row.dtype != target_row.dtype:
+                raise ValueError("draft_row must match target_row")
+        if probs and target_row.dtype != np.float32:
+            raise TypeError("probabilities must be float32")
+        code = PROBS if probs else _dtype_code(target_row)
+        cdf = np.zeros(V, np.float64)
+        S = self.lib.orc_sample_cdf(_ptr(target_row), _ptr(draft_row), code, V, float(temperature),
+                                    _ptr(cdf))
+        return cdf, float(S)
 
     def verify_tree(self, logits, parent, token):
         """logits [B, N, V], parent [B, N], token [B, N]."""
@@ -233,6 +253,10 @@ def verify_greedy(*a, **k):
 
 def verify_rejection(*a, **k):
     return default().verify_rejection(*a, **k)
+
+
+def sample_cdf(*a, **k):
+    return default().sample_cdf(*a, **k)
 
 
 def verify_tree(*a, **k):

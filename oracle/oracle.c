@@ -136,6 +136,29 @@ static void softmax_row(const void *row, int dtype, int32_t V, double T, double 
         p[v] = exp(orc_widen(row, dtype, v) / T - M) / Z;
 }
 
+/* The distribution of the final sample: after a rejection (Q given) the
+ * residual r = max(0, p - q), or p itself when that has no mass; with no
+ * draft row (every draft accepted) r = p.  Returns S = sum_v r_v. */
+static double final_distribution(const double *P, const double *Q, int32_t V, double *r)
+{
+    double S = 0.0;
+    if (Q) {
+        for (int32_t v = 0; v < V; ++v) {
+            double d = P[v] - Q[v];
+            r[v] = d > 0.0 ? d : 0.0;
+            S += r[v];
+        }
+    }
+    if (!Q || S == 0.0) {
+        S = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+            r[v] = P[v];
+            S += r[v];
+        }
+    }
+    return S;
+}
+
 /*
  * Rejection-sampling verification (Leviathan et al.; Chen et al.; cited by
  * [vLLM-03] "1. principle" for keeping the target distribution at T > 0;
@@ -205,22 +228,9 @@ void orc_verify_rejection(const void *target, const void *draftl, int dtype,
 
         /* the final token: residual after a rejection, else the bonus */
         softmax_row(row_ptr(target, dtype, (int64_t)b * (K + 1) + n, row_stride), dtype, V, T, P);
-        double S = 0.0;
-        if (n < len) {
+        if (n < len)
             softmax_row(row_ptr(draftl, dtype, (int64_t)b * K + n, row_stride), dtype, V, T, Q);
-            for (int32_t v = 0; v < V; ++v) {
-                double d = P[v] - Q[v];
-                r[v] = d > 0.0 ? d : 0.0;
-                S += r[v];
-            }
-        }
-        if (n == len || S == 0.0) {
-            S = 0.0;
-            for (int32_t v = 0; v < V; ++v) {
-                r[v] = P[v];
-                S += r[v];
-            }
-        }
+        double S = final_distribution(P, n < len ? Q : NULL, V, r);
         /* tie band for this draw, in probability mass: band_scale times
          * sqrt(sum p^2 + sum q^2) over the rows the final sample reads */
         double sq = 0.0;
@@ -273,6 +283,29 @@ void orc_verify_rejection(const void *target, const void *draftl, int dtype,
     free(P);
     free(Q);
     free(r);
+}
+
+/* The final sample's cumulative distribution for one row pair (the
+ * definition orc_verify_rejection draws from): cdf[v] = C_v = the sum of
+ * r_w over w <= v in token order; returns S = C_{V-1}.  draft_row NULL:
+ * r = p (the bonus). */
+double orc_sample_cdf(const void *target_row, const void *draft_row, int dtype, int32_t V,
+                      double T, double *cdf)
+{
+    double *P = (double *)malloc(sizeof(double) * (size_t)V);
+    double *Q = (double *)malloc(sizeof(double) * (size_t)V);
+    softmax_row(target_row, dtype, V, T, P);
+    if (draft_row)
+        softmax_row(draft_row, dtype, V, T, Q);
+    double S = final_distribution(P, draft_row ? Q : NULL, V, cdf);
+    double C = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+        C += cdf[v];
+        cdf[v] = C;
+    }
+    free(P);
+    free(Q);
+    return S;
 }
 
 /*

@@ -102,6 +102,15 @@ void orc_verify_rejection(const void *target, const void *draftl, int dtype,
                           uint32_t *flags);
 
 /*
+ * The final sample's cumulative distribution for one row pair: r = max(0,
+ * p - q) when draft_row is given (p when that sums to 0), r = p when it is
+ * NULL; cdf[v] = sum_{w <= v} r_w over V entries; returns S = sum_v r_v.
+ * The rows are single rows of dtype (ORC_PROBS: probabilities).
+ */
+double orc_sample_cdf(const void *target_row, const void *draft_row, int dtype, int32_t V,
+                      double T, double *cdf);
+
+/*
  * Tree verification.  logits [B][N][row_stride]: row j scores the children
  * of node j.  parent [B][N] (parent[b][0] = -1, parent[b][j] in [0, j)),
  * token [B][N] (root token ignored).

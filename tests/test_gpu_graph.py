@@ -56,8 +56,7 @@ def test_graph_replay_matches_eager_and_oracle(orc):
         np.testing.assert_array_equal(eager["tree"][k], r[k], err_msg="tree " + k)
     r = orc.verify_rejection(rj["target"], rj["draft_logits"], rj["draft"], rj["uniforms"])
     flagged, mism = check_rejection({k: torch.from_numpy(v) for k, v in eager["rejection"].items()},
-                                    r, "graph eager")
-    assert mism <= flagged
+                                    r, "graph eager", max_flagged=2)
 
     say("graph capture of the four calls")
     g = torch.cuda.CUDAGraph()

@@ -53,8 +53,7 @@ def test_greedy_and_rejection_most_drafts(orc):
     g = sv.verify_rejection(to_dev(rw["target"]), to_dev(rw["draft_logits"]), to_dev(rw["draft"]),
                             to_dev(rw["uniforms"]), 1.0)
     r = orc.verify_rejection(rw["target"], rw["draft_logits"], rw["draft"], rw["uniforms"], 1.0)
-    flagged, mism = check_rejection(g, r, "K4096")
-    assert mism <= flagged
+    check_rejection(g, r, "K4096", max_flagged=1)
 
 
 def test_rejection_vocabulary_past_selection_staging(orc):
@@ -65,8 +64,7 @@ def test_rejection_vocabulary_past_selection_staging(orc):
     g = sv.verify_rejection(to_dev(wl["target"]), to_dev(wl["draft_logits"]), to_dev(wl["draft"]),
                             to_dev(wl["uniforms"]), 1.0)
     r = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], wl["uniforms"], 1.0)
-    flagged, mism = check_rejection(g, r, "V3000001")
-    assert mism <= flagged
+    check_rejection(g, r, "V3000001", max_flagged=1)
 
 
 def test_ngram_longest_proposal(orc):

@@ -26,11 +26,10 @@ def _case(orc, P, Q, draft, u, draft_len=None, label=""):
     g = sv.verify_rejection_probs(to_dev(P), to_dev(Q), to_dev(draft), to_dev(u),
                                   to_dev(draft_len) if draft_len is not None else None, stats=stats)
     r = orc.verify_rejection(P, Q, draft, u, 1.0, draft_len, probs=True)
-    flagged, mism = check_rejection(g, r, label)
+    check_rejection(g, r, label)
     np.testing.assert_array_equal(host(g["flags"]).astype(np.uint32), r["flags"])
     acc = host(g["accepted"]).astype(np.int64)
     assert host(stats)[0] == acc.sum()
-    assert mism <= flagged
     return r
 
 

@@ -30,6 +30,15 @@ REJECTION_PINS = [R.test_worked_example_sampling_form, R.test_flags_and_draft_le
                   lambda o: R.test_output_distribution_chisquare_v8(o, 1),
                   lambda o: R.test_output_distribution_chisquare_v8(o, 3),
                   R.test_identical_draft_accepts_everything, R.test_one_hot_draft_accepts_with_p]
+TIE_PINS = ([lambda o, d=d: R.test_accept_tie_flag_band(o, d)
+             for d in (-3e-7, 3e-7, -9e-7, 9e-7, -1.1e-6, 1.1e-6, -3e-6, 3e-6)] +
+            [R.test_accept_tie_counts_only_decisions_taken] +
+            [lambda o, e=e, f=f: R.test_sample_tie_flag_band_bonus(o, e[0], e[1], f)
+             for e in ((0.5, 0), (0.75, 1), (0.875, 2)) for f in (-1.5, -0.8, 0.8, 1.5)] +
+            [lambda o, f=f: R.test_sample_tie_flag_band_residual(o, f)
+             for f in (-1.25, -0.85, 0.85, 1.25)] +
+            [R.test_sample_tie_at_the_top_of_the_distribution,
+             R.test_flagged_fraction_at_the_rejection_workload_size])
 TREE_PINS = [TN.test_tree_single_node, TN.test_tree_equal_depth_tie_lowest_id,
              TN.test_chain_tree_is_greedy,
              TN.test_random_trees_brute_force]
@@ -58,6 +67,26 @@ MUTANTS = [
     ("final sample uses the first uniform", "double thr = (double)ub[K] * S;",
      "double thr = (double)ub[0] * S;", REJECTION_PINS),
     ("no stop at the first rejection", "stopped = 1;", "stopped = 0;", REJECTION_PINS),
+    ("every accept test flagged", "if (valid && fabs(ui - ratio) < accept_band)", "if (valid)",
+     TIE_PINS),
+    ("accept band ten times wider", "fabs(ui - ratio) < accept_band", "fabs(ui - ratio) < 10.0 * accept_band",
+     TIE_PINS),
+    ("accept ties flagged at invalid ids", "if (valid && fabs(ui - ratio) < accept_band)",
+     "if (fabs(ui - ratio) < accept_band)", TIE_PINS),
+    ("accept ties never flagged", "atie = 1;", "atie = 0;", TIE_PINS),
+    ("sample band a million times wider", "double band = sample_band_scale * sqrt(sq);",
+     "double band = 1e6 * sample_band_scale * sqrt(sq);", TIE_PINS),
+    ("sample band without the square root", "double band = sample_band_scale * sqrt(sq);",
+     "double band = sample_band_scale * sq;", TIE_PINS),
+    ("sample band ignores the draft row",
+     "        if (n < len)\n            for (int32_t v = 0; v < V; ++v)\n                sq += Q[v] * Q[v];\n",
+     "", TIE_PINS),
+    ("every draw flagged", "} else if (thr - lo < band || hi - thr < band) {", "} else if (1) {",
+     TIE_PINS),
+    ("sample band on one side only", "thr - lo < band || hi - thr < band", "hi - thr < band",
+     TIE_PINS),
+    ("sample ties never flagged", "} else if (thr - lo < band || hi - thr < band) {",
+     "} else if (0) {", TIE_PINS),
     ("tree checks the node's own row", "acc[j] = acc[p] && tok[j] == t[p];",
      "acc[j] = acc[p] && tok[j] == t[j];", TREE_PINS),
     ("tree ignores the parent's acceptance", "acc[j] = acc[p] && tok[j] == t[p];",

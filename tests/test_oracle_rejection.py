@@ -289,3 +289,177 @@ def test_probability_input_zero_draft_probability_accepts(orc):
     assert out["accepted"][0] == 1 and out["emitted"][0, 0] == 0
     assert out["emitted"][0, 1] == 1                 # bonus from p_1 = (0.5, 0.5): u 0.7 -> id 1
     assert V == p.shape[-1]
+
+
+# ------------------------------------------------------------- tie flags
+#
+# GPU parity for rejection sampling compares every decision except those the
+# oracle flags as ties, so the flags themselves are pinned here on rows whose
+# probabilities are exact binary fractions (given as probabilities, so p and
+# q are the row values over an exactly representable sum).  An accept test
+# is a tie when |u - p/q| < 1e-6 (the band the problem statement fixes); a
+# final sample is a tie when u*S lies within SAMPLE_BAND_SCALE * sqrt(sum p^2
+# + sum q^2) probability mass of an end of the chosen token's CDF interval
+# (q only after a rejection).  The square roots below are worked by hand.
+
+def _probs(rows):
+    return np.array(rows, np.float32)[None]
+
+
+def _u_at(target, side):
+    """The fp32 uniform nearest target + side, and its exact distance from
+    target (fp64)."""
+    u = np.float32(target + side)
+    return u, abs(float(u) - target)
+
+
+@pytest.mark.parametrize("side", [-3e-7, 3e-7, -9e-7, 9e-7, -1.1e-6, 1.1e-6, -3e-6, 3e-6])
+def test_accept_tie_flag_band(orc, side):
+    """p(x)/q(x) = 0.125/0.25 = 0.5 exactly.  A uniform within 1e-6 of 0.5
+    is flagged whichever way the test goes; one outside is not; the
+    decision itself is u < 0.5 either way."""
+    tl = _probs([[0.5, 0.25, 0.125, 0.125], [0.25, 0.25, 0.25, 0.25]])
+    dl = _probs([[0.25, 0.25, 0.25, 0.25]])
+    u0, dist = _u_at(0.5, side)
+    assert abs(dist - 1e-6) > 5e-8                    # fp32 rounding keeps the side of the band
+    u = np.array([[u0, 0.3]], np.float32)
+    out = orc.verify_rejection(tl, dl, np.array([[2]], np.int32), u, probs=True)
+    assert out["p_draft"][0, 0] == 0.125 and out["q_draft"][0, 0] == 0.25
+    assert out["accepted"][0] == (1 if u0 < np.float32(0.5) else 0)
+    assert out["accept_tie"][0] == (dist < 1e-6)
+    assert not out["sample_tie"][0]
+
+
+def test_accept_tie_counts_only_decisions_taken(orc):
+    """A near-tie uniform at a position after the first rejection, past
+    draft_len, at an out-of-range id (ratio 0 against u = 0) or where the
+    draft has q(x) = 0 (ratio +inf) is not a decision the verifier takes on
+    a ratio: none is flagged.  A clear decision (|u - p/q| >= 1e-3) is not
+    flagged either."""
+    half = [0.25, 0.25, 0.25, 0.25]
+    tl = _probs([[0.5, 0.25, 0.125, 0.125], [0.5, 0.25, 0.125, 0.125], half])
+    dl = _probs([half, half])
+    x = np.array([[2, 2]], np.int32)                  # ratios 0.5 and 0.5
+    cases = [
+        (np.array([[0.9, 0.5 - 1e-7, 0.3]], np.float32), None, 0),   # rejected at 0; 1 not taken
+        (np.array([[0.1, 0.5 - 1e-7, 0.3]], np.float32), np.array([1], np.int32), 1),   # past len
+        (np.array([[0.499, 0.501, 0.3]], np.float32), None, 1),       # clear both ways
+    ]
+    for u, dlen, acc in cases:
+        out = orc.verify_rejection(tl, dl, x, u, draft_len=dlen, probs=True)
+        assert out["accepted"][0] == acc
+        assert not out["accept_tie"][0], (u, dlen)
+    bad = orc.verify_rejection(tl, dl, np.array([[-1, 2]], np.int32),
+                               np.array([[0.0, 0.2, 0.3]], np.float32), probs=True)
+    assert bad["accepted"][0] == 0 and not bad["accept_tie"][0]
+    qz = _probs([[0.0, 0.5, 0.5, 0.0], half])
+    inf = orc.verify_rejection(tl, qz, np.array([[0, 2]], np.int32),
+                               np.array([[0.9999999, 0.9, 0.3]], np.float32), probs=True)
+    assert inf["accepted"][0] >= 1 and not inf["accept_tie"][0]
+    # the same near-tie uniform at position 1 when position 0 is accepted is flagged
+    near = orc.verify_rejection(tl, dl, x, np.array([[0.1, 0.5 - 3e-7, 0.3]], np.float32),
+                                probs=True)
+    assert near["accepted"][0] == 2 and near["accept_tie"][0]
+
+
+# The bonus row p = (1/2, 1/4, 1/8, 1/8): sum p^2 = 1/4 + 1/16 + 2/64 = 11/32,
+# so the band is SCALE * sqrt(11/32); interval ends at 1/2, 3/4, 7/8.
+BONUS_P = [0.5, 0.25, 0.125, 0.125]
+BONUS_ROOT = np.sqrt(11.0 / 32.0)
+
+
+@pytest.mark.parametrize("end,token_below", [(0.5, 0), (0.75, 1), (0.875, 2)])
+@pytest.mark.parametrize("frac", [-1.5, -0.8, 0.8, 1.5])
+def test_sample_tie_flag_band_bonus(orc, end, token_below, frac):
+    """The bonus draw (draft_len 0, r = p, S = 1): u*S placed frac bands
+    from an interval end.  Within the band (|frac| < 1) the draw is flagged,
+    outside it is not; the token is the one whose interval holds u*S."""
+    band = orc.SAMPLE_BAND_SCALE * BONUS_ROOT
+    tl = _probs([BONUS_P])
+    uK, dist = _u_at(end, frac * band)
+    assert abs(dist / band - abs(frac)) < 0.1
+    out = orc.verify_rejection(tl, np.zeros((1, 0, 4), np.float32), np.zeros((1, 0), np.int32),
+                               np.array([[uK]], np.float32), probs=True)
+    assert out["emitted"][0, 0] == (token_below + 1 if frac > 0 else token_below)
+    assert out["sample_tie"][0] == (abs(frac) < 1.0)
+    assert not out["accept_tie"][0]
+
+
+# After a rejection: p = (3/8, 3/8, 1/8, 1/8), q = (1/8, 1/8, 3/8, 3/8):
+# r = (1/4, 1/4, 0, 0), S = 1/2, one interval end inside at 1/4.  sum p^2 =
+# sum q^2 = 2 (9/64) + 2 (1/64) = 5/16, so the band is SCALE * sqrt(5/8); a
+# band without the draft's terms would be SCALE * sqrt(5/16), 0.707 of it.
+RESID_P = [0.375, 0.375, 0.125, 0.125]
+RESID_Q = [0.125, 0.125, 0.375, 0.375]
+RESID_ROOT = np.sqrt(5.0 / 8.0)
+
+
+@pytest.mark.parametrize("frac", [-1.25, -0.85, 0.85, 1.25])
+def test_sample_tie_flag_band_residual(orc, frac):
+    """x = 2 (ratio 1/3) rejected by u = 0.9; the residual is drawn with
+    u_K * S placed frac bands from the interval end 1/4 (u_K near 1/2)."""
+    band = orc.SAMPLE_BAND_SCALE * RESID_ROOT
+    tl = _probs([RESID_P, BONUS_P])
+    dl = _probs([RESID_Q])
+    uK, dist2 = _u_at(0.5, 2.0 * frac * band)           # u_K * S = u_K / 2
+    assert abs(dist2 / 2.0 / band - abs(frac)) < 0.05
+    out = orc.verify_rejection(tl, dl, np.array([[2]], np.int32),
+                               np.array([[0.9, uK]], np.float32), probs=True)
+    assert out["accepted"][0] == 0
+    assert out["emitted"][0, 0] == (1 if frac > 0 else 0)
+    assert out["sample_tie"][0] == (abs(frac) < 1.0)
+    assert not out["accept_tie"][0]
+
+
+def test_sample_tie_at_the_top_of_the_distribution(orc):
+    """u_K = the largest fp32 below 1 puts u*S within 6e-8 of the top of the
+    last token's interval: flagged; u_K = 0 sits at the bottom of the first
+    token's interval: flagged."""
+    tl = _probs([BONUS_P])
+    empty = (np.zeros((1, 0, 4), np.float32), np.zeros((1, 0), np.int32))
+    top = orc.verify_rejection(tl, *empty, np.array([[np.nextafter(np.float32(1), np.float32(0))]],
+                                                    np.float32), probs=True)
+    assert top["emitted"][0, 0] == 3 and top["sample_tie"][0]
+    bottom = orc.verify_rejection(tl, *empty, np.array([[0.0]], np.float32), probs=True)
+    assert bottom["emitted"][0, 0] == 0 and bottom["sample_tie"][0]
+
+
+def test_flagged_fraction_at_the_rejection_workload_size(orc):
+    """On full-size rejection rows (V = 128256, bf16 N(0, 2) target and
+    target + N(0, 0.5) draft) the tie flags mark a small fraction of draws:
+    a band wider than the stated one would flag far more, so the GPU parity
+    tests would compare little.  Uniforms are redrawn over the same rows."""
+    from proposal_sv_verify_amd import workloads as W
+    wl = W.rejection_workload(8, 5, 128256, seed=W.seed_for(3, salt=7))
+    flags = accept = 0
+    trials = 0
+    rng = np.random.default_rng(12)
+    for rep in range(6):
+        u = rng.random((8, 6), dtype=np.float32)
+        out = orc.verify_rejection(wl["target"], wl["draft_logits"], wl["draft"], u)
+        flags += int(out["sample_tie"].sum())
+        accept += int(out["accept_tie"].sum())
+        trials += 8
+    assert accept == 0
+    assert flags <= 0.1 * trials
+
+
+def test_sample_cdf_hand_worked(orc):
+    """The residual of the rows above is (1/4, 1/4, 0, 0) with S = 1/2; with
+    no draft row the CDF is p's; q = p leaves no residual, so p is drawn;
+    S equals the total-variation distance 1 - sum min(p, q) on random rows."""
+    C, S = orc.sample_cdf(np.array(RESID_P, np.float32), np.array(RESID_Q, np.float32), probs=True)
+    assert S == 0.5 and C.tolist() == [0.25, 0.5, 0.5, 0.5]
+    C, S = orc.sample_cdf(np.array(BONUS_P, np.float32), probs=True)
+    assert S == 1.0 and C.tolist() == [0.5, 0.75, 0.875, 1.0]
+    C, S = orc.sample_cdf(np.array(RESID_P, np.float32), np.array(RESID_P, np.float32), probs=True)
+    assert S == 1.0 and C.tolist() == [0.375, 0.75, 0.875, 1.0]
+    rng = np.random.default_rng(13)
+    for T in (0.7, 1.0):
+        t = (2 * rng.standard_normal(500)).astype(np.float32)
+        d = (t + 0.5 * rng.standard_normal(500)).astype(np.float32)
+        C, S = orc.sample_cdf(t, d, T)
+        p, q = _softmax64(t / np.float32(T) if T == 1.0 else t.astype(np.float64) / T), \
+            _softmax64(d / np.float32(T) if T == 1.0 else d.astype(np.float64) / T)
+        assert S == pytest.approx(1.0 - np.minimum(p, q).sum(), rel=1e-12)
+        assert np.all(np.diff(C) >= 0) and C[-1] == S
