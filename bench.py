@@ -38,7 +38,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 LAUNCH_KERNELS = {
     "greedy": "sv_verify_greedy: k_row_argmax<bf16> (2304 rows) + k_greedy_scan",
     "tree": "sv_verify_tree: k_row_argmax<bf16> (2048 rows) + k_tree_scan",
-    "rejection": "sv_verify_rejection: k_rej_stats + k_rej_scan + k_rej_chunks + k_rej_select",
+    "rejection": "sv_verify_rejection: k_rej_stats + k_rej_final + k_rej_select",
 }
 
 KERNEL_SOURCES = {
@@ -609,7 +609,8 @@ def main():
     result = dict(metric=METRIC, value=round(positions * K / wall, 1), unit="verified positions/s",
                   n_gpus=1, steps=K, warmup=args.warmup, ms_per_step=round(ms_step, 4),
                   higher_is_better=True, scaling="weak", vs_baseline=None,
-                  dtype="bf16 logits; f32 exp, f64 sums", data="synthetic",
+                  dtype="bf16 logits (argmax compares in f32); rejection f32 exp and 16-byte-vector sums, "
+                        "f64 across vectors and after", data="synthetic",
                   config=dict(workload="one verify+propose pass: ngram B64 L8192 n5..2 K8; "
                                        "rejection B64 K5 V128256 bf16 T1; greedy B256 K8 V151936 "
                                        "bf16 alpha0.6; tree B32 N64 V128256 bf16",

@@ -49,7 +49,8 @@
  *    NULL): see SV_FLAG_*.
  *  - Workspaces are device scratch for per-row partial results; size one
  *    with the matching sv_*_workspace_bytes() (16-byte aligned).  They need
- *    no initialisation and their contents are undefined after a call.
+ *    no initialisation and their contents are undefined after a call,
+ *    except where a call documents a part of them.
  *    Calls that share a workspace must be ordered on one stream; calls
  *    running concurrently need their own.
  *  - argmax ties resolve to the LOWEST token id (the numpy / torch rule);
@@ -106,15 +107,20 @@ const char *sv_status_string(int status);
 const char *sv_last_error_message(void);
 
 /*
- * Launch tuning of the row-streaming kernels (process-wide, not
- * thread-safe; a value <= 0 restores the default).  Rows are cut into
- * segments so that a call launches about SV_TUNE_TARGET_WORKGROUPS
- * workgroups (default 2048: eight per compute unit) without segments
- * shorter than SV_TUNE_MIN_SEGMENT_BYTES (default 32768).  The rejection
- * statistics kernel works per wave: about 4 * SV_TUNE_TARGET_WORKGROUPS
- * pieces, at most 16 per row, none shorter than a quarter of
- * SV_TUNE_MIN_SEGMENT_BYTES.  Workspace sizes follow the current setting:
- * query them after changing it.
+ * Launch tuning of the row-streaming kernels (process-wide; a value <= 0
+ * restores the default).  Rows are cut into segments so that a call
+ * launches about SV_TUNE_TARGET_WORKGROUPS workgroups (default 2048: eight
+ * per compute unit) without segments shorter than SV_TUNE_MIN_SEGMENT_BYTES
+ * (default 32768).  The rejection statistics kernel works per wave: about
+ * 4 * SV_TUNE_TARGET_WORKGROUPS pieces, at most 16 per row, none shorter
+ * than a quarter of SV_TUNE_MIN_SEGMENT_BYTES.
+ * Thread safety: the setting is atomic, and every call (including the
+ * sv_*_workspace_bytes queries) reads it once and plans from that copy, so
+ * one call never mixes two settings.  Workspace needs follow the setting: a
+ * workspace sized before a change may be too small after it, and the call
+ * then returns SV_ERR_WORKSPACE (it never writes past workspace_bytes).
+ * Results do not depend on the setting except within the rounding band of a
+ * rejection-sampling tie (sums are associated by piece).
  */
 #define SV_TUNE_TARGET_WORKGROUPS 1
 #define SV_TUNE_MIN_SEGMENT_BYTES 2
@@ -172,12 +178,32 @@ int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
  *   p_draft, q_draft [B][K] fp32 or NULL (out: p_i(x_i), q_i(x_i) for
  *              i < len with a valid id, else 0)
  *   flags, stats as for sv_verify_greedy.
- * Arithmetic: exp in fp32 per element, every sum, normaliser, ratio and CDF
- * in fp64; p_i(x_i), q_i(x_i) use fp64 exp.  Decisions agree with an fp64
- * evaluation except within a rounding band of a tie.  A -inf logit has
- * probability 0; every row needs at least one finite logit.
+ * Arithmetic: e^(l/T) per element in fp32 -- for bf16 logits the hardware
+ * exp2 of the exact product l * c1 (c1 = log2(e)/T rounded to 16
+ * significant bits) times (1 + l * k2), the first-order correction for the
+ * rest of the constant; for fp32 logits a Cody-Waite exp (within 1.25 ulp)
+ * -- summed in fp32 over the 8 (bf16) or 4 (fp32) elements of one 16-byte
+ * vector and in fp64 across vectors; normalisers, p/q ratios, the residual,
+ * the masses and the CDF in fp64; p_i(x_i) and q_i(x_i) with an fp64 exp
+ * of the logit at the draft token.  The final sample's per-element
+ * probabilities use the exp their normaliser was summed with.  Decisions
+ * agree with an fp64 evaluation except within a rounding band of a tie: an
+ * accept test with |u - p/q| < 1e-6, a final sample whose u*S lies within
+ * SV_SAMPLE_BAND_SCALE * sqrt(sum p^2 + sum q^2) probability mass of an
+ * end of the chosen token's CDF interval (q only after a rejection).  A
+ * -inf logit has probability 0; every row needs at least one finite logit.
+ * Workspace: sized by sv_rejection_workspace_bytes.  Once the call has
+ * completed, the workspace begins with B * ceil(V / SV_SAMPLE_BLOCK)
+ * sv_sample_mass records: for sequence b, record k holds the masses of r =
+ * max(0, p_n - q_n) (0 after a full acceptance) and of p_n over tokens
+ * [k * SV_SAMPLE_BLOCK, (k + 1) * SV_SAMPLE_BLOCK) of the row pair n the
+ * final sample was drawn from -- the CDF the sample inverted, for callers
+ * that audit the sampling.  The rest of the workspace is undefined.
  * Limits: 1 <= B, 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= SV_MAX_V.
  */
+#define SV_SAMPLE_BLOCK 1024             /* tokens per final-sample mass record */
+#define SV_SAMPLE_BAND_SCALE 1.9073486328125e-06   /* 16 * 2^-23: final-sample tie band */
+
 size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V);
 int sv_verify_rejection(const void *target_logits, const void *draft_logits,
                         int32_t dtype, int64_t row_stride,

@@ -292,10 +292,12 @@ def verify_greedy(*a, **k):
 
 
 def prepare_rejection(target, draft_logits, draft, uniforms, temperature=1.0, draft_len=None, *,
-                      want_probs=True, stats=None):
+                      want_probs=True, stats=None, ws=None):
     """Rejection-sampling verification.  target [B, K+1, V], draft_logits
     [B, K, V] (same dtype and row spacing), draft [B, K] int32, uniforms
-    [B, K+1] float32.  Outputs: accepted, emitted, p_draft, q_draft, flags."""
+    [B, K+1] float32, ws: a uint8 device tensor to use as the workspace
+    (default: the cached one).  Outputs: accepted, emitted, p_draft,
+    q_draft, flags."""
     torch = _torch()
     L = load()
     code, rs = _logits_args(target, "target", 2)
@@ -319,7 +321,11 @@ def prepare_rejection(target, draft_logits, draft, uniforms, temperature=1.0, dr
     qd = torch.empty(B, K, dtype=torch.float32, device=dev) if want_probs else None
     flg = torch.empty(B, dtype=torch.int32, device=dev)
     s = _stream(dev)
-    ws = workspace(L.sv_rejection_workspace_bytes(B, K, V), dev, s)
+    need = L.sv_rejection_workspace_bytes(B, K, V)
+    if ws is None:
+        ws = workspace(need, dev, s)
+    elif ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != dev:
+        raise ValueError("ws must be a contiguous uint8 tensor on the logits' device")
     args = (target.data_ptr(), _ptr(draft_logits) if K > 0 else None, code, rs, _ptr(draft),
             _ptr(draft_len), uniforms.data_ptr(), float(temperature), B, K, V, acc.data_ptr(),
             emi.data_ptr(), _ptr(pd), _ptr(qd), flg.data_ptr(), _ptr(stats), ws.data_ptr(),

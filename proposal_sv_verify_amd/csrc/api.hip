@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -65,25 +66,42 @@ int check_device()
 
 // ---------------------------------------------------------------- planning
 
-// Launch shape of a row-streaming kernel: every row is cut into `segs`
-// segments.  Rows alone fill the grid once there are g_target_wgs of them
-// (8 workgroups per CU on 256 CUs); below that, the segment count is chosen
-// among those giving at least g_target_wgs workgroups (and segments of at
-// least g_min_seg_bytes) so that the workgroups fill whole rounds of the 256
-// compute units as closely as possible.
-int64_t g_target_wgs = 2048;
-int64_t g_min_seg_bytes = 32 * 1024;
+// Launch tuning, process-wide.  Every call reads it once into a Tuning and
+// plans its launch and its workspace need from that copy alone, so a
+// concurrent change can never make one call disagree with itself: a
+// workspace sized before a change that needs more is rejected
+// (SV_ERR_WORKSPACE), never overrun.
+constexpr int64_t kDefaultTargetWgs = 2048;
+constexpr int64_t kDefaultMinSegBytes = 32 * 1024;
+std::atomic<int64_t> g_target_wgs{kDefaultTargetWgs};
+std::atomic<int64_t> g_min_seg_bytes{kDefaultMinSegBytes};
 constexpr int64_t kCUs = 256;
+
+struct Tuning {
+    int64_t target_wgs;
+    int64_t min_seg_bytes;
+};
+
+Tuning tuning_now()
+{
+    return Tuning{g_target_wgs.load(std::memory_order_relaxed), g_min_seg_bytes.load(std::memory_order_relaxed)};
+}
 
 struct RowPlan {
     int segs;
     int seg_len;
 };
 
-RowPlan plan_rows(int64_t rows, int V, int esize)
+// Launch shape of a row-streaming kernel: every row is cut into `segs`
+// segments.  Rows alone fill the grid once there are target_wgs of them
+// (8 workgroups per CU on 256 CUs); below that, the segment count is chosen
+// among those giving at least target_wgs workgroups (and segments of at
+// least min_seg_bytes) so that the workgroups fill whole rounds of the 256
+// compute units as closely as possible.
+RowPlan plan_rows(int64_t rows, int V, int esize, const Tuning &tu)
 {
-    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize / g_min_seg_bytes);
-    const int64_t lo = std::min(by_size, (g_target_wgs + rows - 1) / rows);
+    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize / tu.min_seg_bytes);
+    const int64_t lo = std::min(by_size, (tu.target_wgs + rows - 1) / rows);
     const int64_t hi = std::min(by_size, 2 * lo);
     int64_t segs = lo;
     double best = -1.0;
@@ -105,12 +123,12 @@ RowPlan plan_rows(int64_t rows, int V, int esize)
 
 // Launch shape of the one-wave-per-item rejection statistics kernel: each
 // row is cut into `segs` pieces so that the items about fill the wave slots
-// of the chip (4 * g_target_wgs waves: 32 per CU) in a single round, with
-// pieces of at least g_min_seg_bytes / 4 and at most kMaxSegs per row.
-RowPlan plan_items(int64_t rows, int V, int esize)
+// of the chip (4 * target_wgs waves: 32 per CU) in a single round, with
+// pieces of at least min_seg_bytes / 4 and at most kMaxSegs per row.
+RowPlan plan_items(int64_t rows, int V, int esize, const Tuning &tu)
 {
-    const int64_t slots = 4 * g_target_wgs;
-    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize * 4 / g_min_seg_bytes);
+    const int64_t slots = 4 * tu.target_wgs;
+    const int64_t by_size = std::max<int64_t>(1, static_cast<int64_t>(V) * esize * 4 / tu.min_seg_bytes);
     int64_t segs = std::max<int64_t>(1, slots / rows);
     segs = std::min<int64_t>(segs, std::min<int64_t>(by_size, sv::kMaxSegs));
     int64_t seg_len = (V + segs - 1) / segs;
@@ -134,22 +152,27 @@ ArgLayout arg_layout(int64_t B, int64_t rows_per_seq, const RowPlan &pl)
     return L;
 }
 
+// The rejection workspace: the sub-chunk masses first (their place and size
+// depend on B and V only, so the shard calls that write and read them agree
+// whatever the launch plan), then the statistics partials and the sequence
+// states.
 struct RejLayout {
-    size_t partial, seq, cmass, total;
+    size_t cmass, partial, seq, total;
 };
+
+int64_t sample_blocks(int V) { return (static_cast<int64_t>(V) + sv::kRejSub - 1) / sv::kRejSub; }
 
 RejLayout rej_layout(int64_t B, int64_t K, int V, const RowPlan &pl)
 {
     const int64_t rows = B * (2 * K + 1);
-    const int64_t nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
     RejLayout L{};
     size_t off = 0;
+    L.cmass = off;
+    off = align_up(off + sizeof(sv::ChunkMass) * B * sample_blocks(V));
     L.partial = off;
     off = align_up(off + sizeof(sv::SoftPartial) * rows * pl.segs);
     L.seq = off;
     off = align_up(off + sizeof(sv::SeqState) * B);
-    L.cmass = off;
-    off = align_up(off + sizeof(sv::ChunkMass) * B * nchunks * (sv::kRejChunk / sv::kRejSub));
     L.total = off;
     return L;
 }
@@ -235,11 +258,11 @@ const char *sv_last_error_message(void) { return g_err.c_str(); }
 int sv_set_tuning(int32_t key, int64_t value)
 {
     if (key == SV_TUNE_TARGET_WORKGROUPS) {
-        g_target_wgs = value > 0 ? value : 2048;
+        g_target_wgs.store(value > 0 ? value : kDefaultTargetWgs, std::memory_order_relaxed);
         return SV_OK;
     }
     if (key == SV_TUNE_MIN_SEGMENT_BYTES) {
-        g_min_seg_bytes = value > 0 ? value : 32 * 1024;
+        g_min_seg_bytes.store(value > 0 ? value : kDefaultMinSegBytes, std::memory_order_relaxed);
         return SV_OK;
     }
     return fail(SV_ERR_INVALID_ARG, "unknown tuning key %d", key);
@@ -251,8 +274,9 @@ size_t sv_greedy_workspace_bytes(int32_t B, int32_t K, int32_t V)
 {
     if (B < 1 || K < 0 || V < 1)
         return 0;
-    const RowPlan a = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 2);
-    const RowPlan b = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 4);
+    const Tuning tu = tuning_now();
+    const RowPlan a = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 2, tu);
+    const RowPlan b = plan_rows(static_cast<int64_t>(B) * (K + 1), V, 4, tu);
     const size_t x = arg_layout(B, K + 1, a).total, y = arg_layout(B, K + 1, b).total;
     return x > y ? x : y;
 }
@@ -274,7 +298,7 @@ int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
     if (!accepted || !emitted)
         return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
     const int64_t rows = static_cast<int64_t>(B) * (K + 1);
-    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype), tuning_now());
     const ArgLayout L = arg_layout(B, K + 1, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
@@ -312,8 +336,9 @@ size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V)
 {
     if (B < 1 || N < 1 || V < 1)
         return 0;
-    const RowPlan a = plan_rows(static_cast<int64_t>(B) * N, V, 2);
-    const RowPlan b = plan_rows(static_cast<int64_t>(B) * N, V, 4);
+    const Tuning tu = tuning_now();
+    const RowPlan a = plan_rows(static_cast<int64_t>(B) * N, V, 2, tu);
+    const RowPlan b = plan_rows(static_cast<int64_t>(B) * N, V, 4, tu);
     const size_t x = arg_layout(B, N, a).total, y = arg_layout(B, N, b).total;
     return x > y ? x : y;
 }
@@ -343,7 +368,7 @@ int sv_verify_tree(const void *logits, int32_t dtype, int64_t row_stride,
     if (!accepted || !path || !emitted)
         return fail(SV_ERR_INVALID_ARG, "accepted, path and emitted are required");
     const int64_t rows = static_cast<int64_t>(B) * N;
-    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype), tuning_now());
     const ArgLayout L = arg_layout(B, N, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
@@ -386,8 +411,9 @@ size_t sv_argmax_shard_workspace_bytes(int32_t rows, int32_t V)
 {
     if (rows < 1 || V < 1)
         return 0;
-    const RowPlan a = plan_rows(rows, V, 2);
-    const RowPlan b = plan_rows(rows, V, 4);
+    const Tuning tu = tuning_now();
+    const RowPlan a = plan_rows(rows, V, 2, tu);
+    const RowPlan b = plan_rows(rows, V, 4, tu);
     const size_t x = arg_layout(1, rows, a).total, y = arg_layout(1, rows, b).total;
     return x > y ? x : y;
 }
@@ -411,7 +437,7 @@ int sv_argmax_shard(const void *logits, int32_t dtype, int64_t row_stride,
         return st;
     if (!out || misaligned(out, 8))
         return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
-    const RowPlan pl = plan_rows(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_rows(rows, V, esize_of(dtype), tuning_now());
     const ArgLayout L = arg_layout(1, rows, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
@@ -571,6 +597,7 @@ void set_rows(sv::RejectParams &p, const void *target_logits, const void *draft_
     p.V = V;
     p.v_full = V;
     p.nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
+    p.nsub = static_cast<int32_t>(sample_blocks(V));
     const int64_t esize = esize_of(dtype);
     p.vec_ok = !misaligned(target_logits, 16) && (K == 0 || !misaligned(draft_logits, 16)) &&
                (row_stride * esize) % 16 == 0 && V % (16 / esize) == 0;
@@ -590,8 +617,9 @@ size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V)
     if (B < 1 || K < 0 || V < 1)
         return 0;
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RowPlan a = plan_items(rows, V, 2);
-    const RowPlan b = plan_items(rows, V, 4);
+    const Tuning tu = tuning_now();
+    const RowPlan a = plan_items(rows, V, 2, tu);
+    const RowPlan b = plan_items(rows, V, 4, tu);
     const size_t x = rej_layout(B, K, V, a).total, y = rej_layout(B, K, V, b).total;
     return x > y ? x : y;
 }
@@ -624,7 +652,7 @@ int rejection_call(const void *target_logits, const void *draft_logits,
     if (!accepted || !emitted)
         return fail(SV_ERR_INVALID_ARG, "accepted and emitted are required");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RowPlan pl = plan_items(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_items(rows, V, esize_of(dtype), tuning_now());
     const RejLayout L = rej_layout(B, K, V, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
@@ -701,6 +729,7 @@ int sv_verify_rejection_probs(const float *target_probs, const float *draft_prob
 static_assert(sizeof(sv_softmax_partial) == sizeof(sv::SoftPartial), "partial layout");
 static_assert(sizeof(sv_rejection_state) == sizeof(sv::SeqState), "state layout");
 static_assert(sizeof(sv_sample_mass) == sizeof(sv::ChunkMass), "mass layout");
+static_assert(SV_SAMPLE_BLOCK == sv::kRejSub, "the documented mass records are the sub-chunk masses");
 static_assert(SV_MAX_REJECT_SHARDS <= sv::kMaxSegs, "shards merge like row segments");
 
 namespace {
@@ -756,7 +785,7 @@ int sv_rejection_shard_stats(const void *target_logits, const void *draft_logits
     if (!out || misaligned(out, 8))
         return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RowPlan pl = plan_items(rows, V, esize_of(dtype));
+    const RowPlan pl = plan_items(rows, V, esize_of(dtype), tuning_now());
     const RejLayout L = rej_layout(B, K, V, pl);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
@@ -852,7 +881,7 @@ int sv_rejection_shard_mass(const void *target_logits, const void *draft_logits,
     if (!out || misaligned(out, 8))
         return fail(SV_ERR_INVALID_ARG, "out must be non-NULL and 8-byte aligned");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype)));
+    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype), tuning_now()));
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
     const int nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
@@ -900,7 +929,7 @@ int sv_rejection_shard_sample(const void *target_logits, const void *draft_logit
     if (!emitted)
         return fail(SV_ERR_INVALID_ARG, "emitted is NULL");
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
-    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype)));
+    const RejLayout L = rej_layout(B, K, V, plan_items(rows, V, esize_of(dtype), tuning_now()));
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
     if ((st = check_device()) != SV_OK)
@@ -933,11 +962,12 @@ int sv_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream)
         return fail(SV_ERR_INVALID_ARG, "buf and out are required");
     if (bytes < 16 || bytes % 16 != 0 || misaligned(buf, 16))
         return fail(SV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and buf 16-byte aligned");
-    if (bytes / 4 > (static_cast<size_t>(1) << 30) * static_cast<size_t>(g_target_wgs))
+    const int64_t wgs = tuning_now().target_wgs;
+    if (bytes / 4 > (static_cast<size_t>(1) << 30) * static_cast<size_t>(wgs))
         return fail(SV_ERR_UNSUPPORTED, "bytes too large");
     if ((st = check_device()) != SV_OK)
         return st;
-    hipError_t e = sv::launch_read_probe(buf, static_cast<int64_t>(bytes), out, g_target_wgs,
+    hipError_t e = sv::launch_read_probe(buf, static_cast<int64_t>(bytes), out, static_cast<int>(wgs),
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "probe launch");

@@ -6,32 +6,29 @@
 // target rows and K draft rows of every sequence streams the logits once
 // with 16-byte loads (the pieces are sized so that every wave of the launch
 // is resident at once).  Each lane sums exp(l / T) against the fixed
-// reference 0 (fp32 sums of 8 terms, fp64 across them).  For bf16 logits
-// the hardware exp2 takes the exact product of l and log2(e)/T rounded to
-// 16 bits, and the rounding is corrected to first order through a second
-// sum, of the terms weighted by l; fp32 logits use the compensated exp
-// (about one ulp either way).  The rare vectors whose fp32 sum leaves a
-// wide range (logits above about 44 T, -inf entries, rows far below 0) go
-// through a careful path with its own reference and fp64 rescales.  The
-// wave combines its lanes onto their largest reference and writes
-// (reference, sum).
+// reference 0: fp32 sums of the 8 terms of a 16-byte vector, fp64 across
+// vectors.  For bf16 logits the hardware exp2 takes the exact product of l
+// and log2(e)/T rounded to 16 bits, and the rounding is corrected to first
+// order through a second fp32 sum, of the terms weighted by l; fp32 logits
+// use the compensated exp (about one ulp either way).  The rare vectors
+// whose fp32 sum leaves a wide range (logits above about 44 T, -inf
+// entries, rows far below 0) go through a careful path with its own
+// reference and fp64 rescales.  The wave combines its lanes onto their
+// largest reference and writes (reference, sum), with the logit at the
+// row's draft token when the piece holds it.
 //
-// Kernel 2 (accept scan).  One workgroup per sequence: merge the segment
-// statistics of each row in LDS, with the logits at the draft tokens that
-// the statistics kernel captured, then one lane per draft position computes
-// p_k(x_k) and q_k(x_k) with fp64 exp and the test u_k < p/q in fp64; a
-// ballot of the rejections gives the first one, n.  The lane at position n
-// publishes the statistics of row pair n.  (Running this inside kernel 3's
-// workgroups instead was measured slower, 18.5-19.7 us against 5 + 9.6 us:
-// every chunk then waits out the whole decision before loading its data.)
+// Kernel 2 (accept decision and final-sample masses).  One workgroup per
+// (sequence, 4096-element chunk).  Wave 0 merges the statistics of the
+// sequence's rows and takes the accept decision: per draft position p_k(x_k)
+// and q_k(x_k) with an fp64 exp, the test u_k < p/q in fp64, a ballot of the
+// rejections for the first one, n (the workgroup of chunk 0 also writes the
+// per-sequence outputs).  The final token is drawn from one row pair: r =
+// max(0, p_n - q_n) after a rejection (p_n when that sums to zero), or p_n
+// when every draft was accepted.  Every wave then forms p and r per element
+// of its 1024-element sub-chunk of that pair (the statistics kernel's exp,
+// fp64 after it) and publishes the sub-chunk's masses.
 //
-// Kernel 3 (final-sample masses).  The final token is drawn from one row
-// pair: r = max(0, p_n - q_n) after a rejection (p_n when that sums to
-// zero), or p_n when every draft was accepted.  One workgroup per (sequence,
-// 4096-element chunk) forms p and r per element (fp32 exp, fp64 after);
-// each wave publishes the masses of its 1024-element sub-chunk.
-//
-// Kernel 4 (selection).  One workgroup per sequence prefix-sums the
+// Kernel 3 (selection).  One workgroup per sequence prefix-sums the
 // sub-chunk masses to find the sub-chunk where the running mass first
 // exceeds u_K * S, then scans that sub-chunk in token order for the token
 // whose cumulative mass first exceeds it, and writes the emitted tokens.
@@ -83,17 +80,42 @@ struct LaneSums {
     float rc = -__builtin_inff();
 };
 
-// The careful path for n values whose fast fp32 sum `s` is out of range.
-template <bool kUnitT, int n>
-__device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSums &ls, float inv_t,
-                                            double inv_t_d)
+// How the fast path forms e^(l/T).
+enum ExpMode : int {
+    kExpUnitT = 0,    // compensated exp of l (T == 1)
+    kExpScaled = 1,   // compensated exp of l * (1/T)
+    kExpSplit = 2,    // bf16 only: split constant, first-order correction summed apart
+    kProbs = 3,       // the values are probabilities: summed as they are
+};
+
+// e^(f / T) of one value by the fast path's arithmetic, -inf giving 0.
+// kExpSplit: f is clamped to a finite value whose exp2 underflows, so the
+// first-order correction stays finite.
+template <int kMode>
+__device__ __forceinline__ float one_term(float f, float inv_t, float c1, float k2)
 {
-    // -inf values made the sum NaN: the same sum with -inf read as 0
+    if constexpr (kMode == kExpSplit) {
+        const float fc = fmaxf(f, -3.0e38f);
+        const float e = __builtin_amdgcn_exp2f(fc * c1);
+        return __builtin_fmaf(e, k2 * fc, e);
+    } else {
+        return exp_cz(kMode == kExpUnitT ? f : f * inv_t);
+    }
+}
+
+// The careful path for n values whose fast fp32 sum `s` is out of range.
+template <int kMode, int n>
+__device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSums &ls, float inv_t,
+                                            double inv_t_d, float c1, float k2)
+{
+    constexpr bool kUnitT = kMode == kExpUnitT;
+    // -inf values made the sum NaN: the same sum, by the same arithmetic,
+    // with -inf read as 0
     if (!(s == s)) {
         s = 0.0f;
 #pragma unroll
         for (int j = 0; j < n; ++j)
-            s += exp_cz(kUnitT ? f[j] : f[j] * inv_t);
+            s += one_term<kMode>(f[j], inv_t, c1, k2);
     }
     // in range, or too small to matter next to what z0 already holds
     if ((s >= kTiny || (s >= 0.0f && ls.z0 >= 1.0)) && s <= kBig) {
@@ -117,14 +139,6 @@ __device__ __forceinline__ void careful_add(const float (&f)[n], float s, LaneSu
         ls.zc += rescale(static_cast<double>(t), vm, ls.rc, inv_t_d);
     }
 }
-
-// How the fast path forms e^(l/T).
-enum ExpMode : int {
-    kExpUnitT = 0,    // compensated exp of l (T == 1)
-    kExpScaled = 1,   // compensated exp of l * (1/T)
-    kExpSplit = 2,    // bf16 only: split constant, first-order correction summed apart
-    kProbs = 3,       // the values are probabilities: summed as they are
-};
 
 // Sum of e^(f_j / T) over a vector, in fp32.  kExpSplit: with log2(e)/T =
 // c1 + c2, c1 of 16 significant bits, y = f c1 is exact for bf16 f, and
@@ -168,7 +182,6 @@ __device__ __forceinline__ float vec_exp_sum(const float (&f)[n], float inv_t, f
 template <typename E, int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_stats(const RejectParams p)
 {
-    constexpr bool kUnitT = kMode == kExpUnitT;
     const int lane = threadIdx.x & 63;
     const int K = p.K;
     const int rows_per_seq = 2 * K + 1;
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
                 if (kMode == kProbs || (s >= kTiny && s <= kBig))
                     ls.z0 += static_cast<double>(s);
                 else
-                    careful_add<kUnitT>(f, s, ls, inv_t, inv_t_d);
+                    careful_add<kMode>(f, s, ls, inv_t, inv_t_d, c1, k2);
             },
             [&](float x, int) {
                 const float f1[1] = {x};
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
                 if (kMode == kProbs || (s >= kTiny && s <= kBig)) {
                     ls.z0 += static_cast<double>(s);
                 } else {
-                    careful_add<kUnitT>(f1, s, ls, inv_t, inv_t_d);
+                    careful_add<kMode>(f1, s, ls, inv_t, inv_t_d, c1, k2);
                 }
             });
         const int xl = x - p.v_offset;
@@ -274,194 +287,149 @@ __global__ __launch_bounds__(kThreads) void k_rej_shard_rows(const RejectParams 
 // inside a branch or loop is waited for on the spot, and each such wait costs
 // a full memory round trip.
 
-// The accept decision of one sequence (steps a4 and the choice of row pair
-// for a5), run by a whole workgroup: draft positions in blocks of 64.  A
-// block needs the statistics of its target rows and draft rows: their
-// segment partials are staged in LDS, each row's maximum is found, every
-// partial is moved onto it (the fp64 rescales run in parallel, one thread per
-// partial) and the row sums are formed; then wave 0 runs the accept test with
-// one lane per position.  In LDS, target row base + i sits at slot i and
-// draft row base + i at slot D0 + i, D0 = min(64, K + 1): for K < 64 the rows
-// are packed (2K + 1 of them).  With `publish` the workgroup also writes the
-// call's per-sequence outputs and the sequence state; every thread gets the
-// state back.  The logits at the draft tokens come with the partials (the
-// statistics kernel captures them); the "segments" are a row's pieces, or
-// its vocabulary shards.
-constexpr int kScanRows = 128;                                 // LDS row slots, at most
-constexpr int kScanPer = kScanRows * kMaxSegs / kThreads;      // partials per thread, at most
-
-__host__ __device__ constexpr int scan_rows(int K) { return (K + 1 < 64 ? K + 1 : 64) + (K < 64 ? K : 64); }
-
-__host__ __device__ constexpr size_t scan_lds_bytes(int K, int segs)
+// A lane's value in every lane (uniform source lane `l`).
+__device__ __forceinline__ double read_lane(double x, int l)
 {
-    return static_cast<size_t>(scan_rows(K)) * (segs * 16 + 16) + sizeof(SeqState);
+    const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffu), l));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), l));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
-struct ScanLds {
-    double *z;      // [rows * segs]
-    double *Z;      // [rows]
-    float *m;       // [rows * segs]
-    float *M;       // [rows]
-    float *lxs;     // [rows * segs] captured logits at the draft tokens (shard input)
-    float *lx;      // [rows]
-    SeqState *seq;
-
-    __device__ ScanLds(char *base, int K, int segs)
-    {
-        const int rows = scan_rows(K);
-        z = reinterpret_cast<double *>(base);
-        Z = z + static_cast<size_t>(rows) * segs;
-        seq = reinterpret_cast<SeqState *>(Z + rows);
-        m = reinterpret_cast<float *>(seq + 1);
-        M = m + static_cast<size_t>(rows) * segs;
-        lxs = M + rows;
-        lx = lxs + static_cast<size_t>(rows) * segs;
-    }
-};
-
-__device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool publish, const ScanLds &S,
-                                           int &len_out)
+__device__ __forceinline__ float read_lane(float x, int l)
 {
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const bool lead = t < 64;                 // wave 0 runs the per-position test
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// The accept decision of one sequence (step a4, and the choice of the row
+// pair step a5 draws from), taken by one wave over blocks of 8 draft
+// positions.  Four lanes hold each row of a block: lane h * 16 + j, j < 8,
+// target row base + j, and lane h * 16 + 8 + j draft row base + j, where
+// quarter h takes the row's partials (pieces of the row, or its vocabulary
+// shards) s = h, h + 4, ...  Each quarter moves its partials onto their
+// largest reference and the quarters combine in fp64.  The draft row's
+// statistics then move to its position's lane, and the lanes of positions
+// below the draft length test u < p/q in fp64 (p and q from the logits at
+// the draft token, which the statistics kernel captured, with an fp64 exp).
+// A ballot of the rejections gives the first one, n; after a block with no
+// rejection that holds the draft length, n is the length (the bonus row).
+// With `publish` the wave writes the call's per-sequence outputs for every
+// position and the sequence state; without, it stops at the block holding
+// n.  The state comes back in every lane.
+constexpr int kDecBlock = 8;
+constexpr int kDecSplit = 4;                      // lanes per row
+constexpr int kDecPer = kMaxSegs / kDecSplit;     // partials per lane, at most
+static_assert(2 * kDecBlock * kDecSplit == 64, "one wave holds a block's rows");
+
+__device__ __forceinline__ SeqState wave_decide(const RejectParams &p, int b, bool publish)
+{
+    const int lane = threadIdx.x & 63;
     const int K = p.K;
     const int segs = p.segs;
-    const int D0 = K + 1 < 64 ? K + 1 : 64;
     const int64_t row0 = static_cast<int64_t>(b) * (2 * K + 1);
-    int n = -1;                               // known to wave 0
-    bool oor = false;
+    const int h = lane >> 4;                  // which quarter of the row's partials
+    const int slot = lane & 15;               // the lane's row in the block
+    const bool tgt = slot < kDecBlock;
+    const int j = slot & (kDecBlock - 1);
     unsigned fl = 0;
-    int len = K;
-    for (int base = 0; base <= K; base += 64) {
-        const int nt = min(64, K + 1 - base);            // target rows of this block
-        const int nd = max(0, min(64, K - base));        // draft rows of this block
-        const int cnt = (nt + nd) * segs;
-        const int k = base + lane;
-        const int kc = max(0, min(k, K - 1));
-        // the draft token first, so its logits can follow it (every wave
-        // loads them; wave 0 uses them)
-        const int x = p.draft[static_cast<int64_t>(b) * K + kc];
-        // every thread: its partials of the block's rows
-        SoftPartial q[kScanPer];
+    const int len = p.has_len ? clamp_len(p.draft_len[b], K, fl) : K;
+    SeqState st{};
+    int n = -1;
+    bool oor = false;
+    for (int base = 0; base <= K; base += kDecBlock) {
+        const int i = base + j;
+        const bool has_row = tgt ? i <= K : i < K;
+        const bool use = has_row && (tgt ? i <= len : i < len);
+        // the row within the sequence, clamped onto an existing one
+        const int ri = min(tgt ? min(i, K) : K + 1 + max(0, min(i, K - 1)), 2 * K);
+        const int x = p.draft[static_cast<int64_t>(b) * K + max(0, min(i, K - 1))];
+        const float u = p.u[static_cast<int64_t>(b) * (K + 1) + min(i, K)];
+        SoftPartial q[kDecPer];
 #pragma unroll
-        for (int j = 0; j < kScanPer; ++j) {
-            const int ci = min(t + j * kThreads, cnt - 1);
-            const int rc = ci / segs;
-            const int s = ci - rc * segs;
-            const int ri = rc < nt ? base + rc : K + 1 + base + (rc - nt);   // row within the sequence
-            q[j] = p.partial[(row0 + ri) * p.part_row_step + s * p.part_seg_step];
+        for (int k = 0; k < kDecPer; ++k)
+            q[k] = p.partial[(row0 + ri) * p.part_row_step +
+                             min(h + kDecSplit * k, segs - 1) * p.part_seg_step];
+        float M = -__builtin_inff();
+        float lx = __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < kDecPer; ++k) {
+            if (h + kDecSplit * k < segs) {
+                M = fmaxf(M, q[k].m);
+                if (q[k].lx == q[k].lx)
+                    lx = q[k].lx;
+            }
         }
+#pragma unroll
+        for (int off = 16; off < 64; off <<= 1) {
+            M = fmaxf(M, __shfl_xor(M, off, 64));
+            const float o = __shfl_xor(lx, off, 64);
+            if (!(lx == lx))
+                lx = o;
+        }
+        double Z = 0.0;
+#pragma unroll
+        for (int k = 0; k < kDecPer; ++k)
+            if (h + kDecSplit * k < segs)
+                Z += q[k].m == M ? q[k].z : rescale(q[k].z, q[k].m, M, p.inv_t_d);
+        Z += __shfl_xor(Z, 16, 64);
+        Z += __shfl_xor(Z, 32, 64);
+        if (!use) {
+            M = -__builtin_inff();
+            Z = 0.0;
+            lx = __builtin_nanf("");
+        }
+        const double Zd = __shfl(Z, lane + kDecBlock, 64);     // lanes of target rows: their draft row
+        const float Md = __shfl(M, lane + kDecBlock, 64);
+        const float lxd = __shfl(lx, lane + kDecBlock, 64);
+        const bool test = lane < kDecBlock && i < len;      // one lane per position
         const bool valid = K > 0 && x >= 0 && x < p.v_full;
-        const int xc = valid ? x : 0;
-        (void)xc;
-        const int len_raw = p.draft_len[b];
-        len = p.has_len ? clamp_len(len_raw, K, fl) : K;
-#pragma unroll
-        for (int j = 0; j < kScanPer; ++j) {
-            const int ci = t + j * kThreads;
-            if (ci < cnt) {
-                const int rc = ci / segs;
-                const int s = ci - rc * segs;
-                const bool tgt = rc < nt;
-                const int kk = base + (tgt ? rc : rc - nt);
-                const bool use = tgt ? kk <= len : kk < len;
-                const int slot = (tgt ? rc : D0 + rc - nt) * segs + s;
-                S.m[slot] = use ? q[j].m : -__builtin_inff();
-                S.z[slot] = use ? q[j].z : 0.0;
-                S.lxs[slot] = use ? q[j].lx : __builtin_nanf("");
-            }
-        }
-        __syncthreads();
-        const int srow = t < nt ? t : (t >= D0 && t < D0 + nd ? t : -1);   // an LDS row slot, or none
-        if (srow >= 0) {
-            float M = -__builtin_inff();
-            float l = __builtin_nanf("");
-            for (int s = 0; s < segs; ++s) {
-                M = fmaxf(M, S.m[srow * segs + s]);
-                const float c = S.lxs[srow * segs + s];
-                if (c == c)
-                    l = c;
-            }
-            S.M[srow] = M;
-            S.lx[srow] = l;
-        }
-        __syncthreads();
-        for (int ci = t; ci < cnt; ci += kThreads) {
-            const int rc = ci / segs;
-            const int s = ci - rc * segs;
-            const int slot_row = rc < nt ? rc : D0 + rc - nt;
-            const int slot = slot_row * segs + s;
-            const float m = S.m[slot];
-            const float M = S.M[slot_row];
-            if (m != M)
-                S.z[slot] = rescale(S.z[slot], m, M, p.inv_t_d);
-        }
-        __syncthreads();
-        if (srow >= 0) {
-            double Z = 0.0;
-            for (int s = 0; s < segs; ++s)
-                Z += S.z[srow * segs + s];
-            S.Z[srow] = Z;
-        }
-        __syncthreads();
-        if (lead) {
-            oor |= k < len && !valid;
-            const bool has_t = lane < nt, has_d = lane < nd;
-            const double zt = has_t ? S.Z[lane] : 0.0, zd = has_d ? S.Z[D0 + lane] : 0.0;
-            const float mt = has_t ? S.M[lane] : 0.0f, md = has_d ? S.M[D0 + lane] : 0.0f;
-            const float lt = has_t ? S.lx[lane] : 0.0f;
-            const float ld = has_d ? S.lx[D0 + lane] : 0.0f;
-            double pk = 0.0, qk = 0.0;
-            bool rejected = false;
-            if (k < len) {
-                double ratio = 0.0;
-                if (valid) {
-                    if (p.probs) {              // given probabilities: value over the row's sum
-                        pk = static_cast<double>(lt) / zt;
-                        qk = static_cast<double>(ld) / zd;
-                    } else {
-                        pk = exp((static_cast<double>(lt) - static_cast<double>(mt)) * p.inv_t_d) / zt;
-                        qk = exp((static_cast<double>(ld) - static_cast<double>(md)) * p.inv_t_d) / zd;
-                    }
-                    ratio = qk > 0.0 ? pk / qk : __builtin_inf();
+        double pk = 0.0, qk = 0.0;
+        bool rejected = false;
+        if (test) {
+            double ratio = 0.0;
+            if (valid) {
+                if (p.probs) {                 // given probabilities: value over the row's sum
+                    pk = static_cast<double>(lx) / Z;
+                    qk = static_cast<double>(lxd) / Zd;
+                } else {
+                    pk = exp((static_cast<double>(lx) - static_cast<double>(M)) * p.inv_t_d) / Z;
+                    qk = exp((static_cast<double>(lxd) - static_cast<double>(Md)) * p.inv_t_d) / Zd;
                 }
-                rejected = !(static_cast<double>(p.u[static_cast<int64_t>(b) * (K + 1) + k]) < ratio);
+                ratio = qk > 0.0 ? pk / qk : __builtin_inf();
             }
-            if (publish && k < K) {
-                if (p.p_draft)
-                    p.p_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(pk);
-                if (p.q_draft)
-                    p.q_draft[static_cast<int64_t>(b) * K + k] = static_cast<float>(qk);
-            }
-            const unsigned long long rej = __ballot(rejected);
+            rejected = !(static_cast<double>(u) < ratio);
+            oor = oor || !valid;
+        }
+        if (publish && lane < kDecBlock && i < K) {
+            if (p.p_draft)
+                p.p_draft[static_cast<int64_t>(b) * K + i] = static_cast<float>(pk);
+            if (p.q_draft)
+                p.q_draft[static_cast<int64_t>(b) * K + i] = static_cast<float>(qk);
+        }
+        const unsigned long long rej = __ballot(rejected);
+        if (n < 0) {
             int here = -1;
-            if (n < 0) {
-                if (rej)
-                    here = base + __builtin_ctzll(rej);
-                else if (len < base + 64)
-                    here = len;               // every draft accepted: the bonus row
-            }
-            if (here >= 0 && k == here) {
-                SeqState sq{};
-                sq.n = here;
-                sq.len = len;
-                sq.zt = zt;
-                sq.mt = mt;
-                if (here < len) {
-                    sq.zd = zd;
-                    sq.md = md;
-                }
-                *S.seq = sq;
-                if (publish)
-                    p.seq[b] = sq;
-            }
-            if (n < 0)
+            if (rej)
+                here = base + __builtin_ctzll(rej);
+            else if (len < base + kDecBlock)
+                here = len;
+            if (here >= 0) {
+                const int l = here - base;
                 n = here;
+                st.n = here;
+                st.len = len;
+                st.zt = read_lane(Z, l);
+                st.mt = read_lane(M, l);
+                if (here < len) {
+                    st.zd = read_lane(Zd, l);
+                    st.md = read_lane(Md, l);
+                }
+            }
         }
-        __syncthreads();                      // LDS is restaged by the next block
+        if (n >= 0 && !publish)
+            break;
     }
-    if (publish && lead) {
+    if (publish) {
         if (__ballot(oor))
             fl |= SV_FLAG_DRAFT_OOR;
         if (lane == 0) {
@@ -473,22 +441,22 @@ __device__ __forceinline__ SeqState decide(const RejectParams &p, int b, bool pu
                 stats_add(p.stats + 1, len);
                 stats_add(p.stats + 2, n + 1);
             }
+            p.seq[b] = st;
         }
         if (p.stats)
             for (int k = lane; k < n; k += 64)
                 stats_add(p.stats + 3 + k, 1);
     }
-    len_out = len;
-    return *S.seq;                            // written before the last barrier
+    return st;
 }
 
-// Kernel 2: the accept decision, one workgroup per sequence.
+// The accept decision alone (the vocabulary-shard call, on every shard's
+// partials): one wave per sequence, four sequences per workgroup.
 __global__ __launch_bounds__(kThreads) void k_rej_scan(const RejectParams p)
 {
-    extern __shared__ __align__(16) char s_dyn[];
-    const ScanLds S(s_dyn, p.K, p.segs);
-    int len;
-    decide(p, blockIdx.x, true, S, len);
+    const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (b < p.B)
+        wave_decide(p, b, true);
 }
 
 // kN consecutive elements [v0, v0 + kN) of a row, loaded before use.  kVec:
@@ -541,16 +509,31 @@ struct Slice {
 };
 
 // The rows of the final sample and the per-element masses over a thread's
-// kN contiguous elements [v0, v0 + cnt).
+// kN contiguous elements [v0, v0 + cnt).  Each element's e^((l - m)/T) is
+// formed the way the statistics kernel formed the normaliser it is divided
+// by: for bf16 logits summed with the split constant against the reference
+// 0, the hardware exp2 of the exact product l c1 with the first-order
+// correction (1 + l k2); otherwise the compensated exp.  The normalised
+// values then carry the exp's rounding only as independent per-element
+// errors, whatever its bias, and the residual max(0, p - q) is not skewed by
+// one row's normaliser against the other's.
+//
+// The per-element work is fp32 on the unnormalised terms: p_j Z_t = e_j and
+// r_j Z_t = max(0, e_j - kappa d_j) with kappa = Z_t / Z_d carried as two
+// fp32 parts (hi + lo, folded in by two FMAs, so the draft row is scaled to
+// about 2^-48 and not to fp32's 2^-24, which would shift r coherently).
+// Sums of terms are scaled by 1 / Z_t in fp64.
 template <typename E>
 struct SampleRows {
     const E *pt;
     const E *pd;        // the target row again when sampling the bonus
     bool residual;      // a draft row is present: r is formed
-    bool probs;         // the rows are probabilities: p_j = value / Z
+    bool probs;         // the rows are probabilities: the terms are the values
+    bool split;         // split-constant exp (bf16, both references 0)
     float mt, md;
-    double izt, izd;
-    float inv_t;
+    double izt;         // 1 / Z_t
+    float kap_hi, kap_lo;
+    float inv_t, c1, k2;
     int V;
 
     __device__ __forceinline__ SampleRows(const RejectParams &p, int b, int len, const SeqState &st)
@@ -560,42 +543,63 @@ struct SampleRows {
         mt = st.mt;
         izt = 1.0 / st.zt;
         inv_t = p.inv_t;
+        c1 = p.split_c1;
+        k2 = p.split_k2;
         V = p.V;
         probs = p.probs != 0;
         residual = n < len;
         pd = pt;
         md = 0.0f;
-        izd = 0.0;
+        kap_hi = kap_lo = 0.0f;
         if (residual) {
             pd = static_cast<const E *>(p.draftl) + (static_cast<int64_t>(b) * K + n) * p.row_stride;
             md = st.md;
-            izd = 1.0 / st.zd;
+            const double kap = st.zt / st.zd;
+            kap_hi = static_cast<float>(kap);
+            kap_lo = static_cast<float>(kap - static_cast<double>(kap_hi));
         }
+        split = sizeof(E) == 2 && p.split_ok && !probs && mt == 0.0f && md == 0.0f;
     }
 
-    // visit(j, p_j, r_j) for j < cnt in order: p_j = exp((l - M) / T) / Z
-    // (fp32 exp, fp64 after), or value / Z for probabilities; after a rejection r_j = max(0, p_j - q_j),
-    // with no draft row r_j = 0.  Both rows are loaded before either is used.
+    // e^((l - m) / T) (the value itself for probabilities), -inf giving 0
+    // (split: l clamped to a finite value whose exp2 underflows, so the
+    // correction term stays finite)
+    __device__ __forceinline__ float term(float l, float m) const
+    {
+        if (probs)
+            return l;
+        if (split) {
+            const float lc = fmaxf(l, -3.0e38f);
+            const float e = __builtin_amdgcn_exp2f(lc * c1);
+            return __builtin_fmaf(e, k2 * lc, e);
+        }
+        return exp_cz((l - m) * inv_t);
+    }
+
+    // visit(j, a_j, r_j) for j < cnt in order, with a_j = p_j Z_t and, after
+    // a rejection, r_j = max(0, p_j - q_j) Z_t (else 0), in fp32.  Both rows
+    // are loaded before either is used.
     template <int kN, bool kVec, typename F>
     __device__ __forceinline__ void visit(int v0, int cnt, F &&f) const
     {
         Slice<E, kN, kVec> st, sd;
         st.fetch(pt, v0, V);
-        sd.fetch(pd, v0, V);
+        if (residual)
+            sd.fetch(pd, v0, V);
         float ft[kN], fd[kN];
         st.widen(ft);
-        sd.widen(fd);
+        if (residual)
+            sd.widen(fd);
 #pragma unroll
         for (int j = 0; j < kN; ++j) {
             if (j < cnt) {
-                const double a = probs ? static_cast<double>(ft[j]) * izt
-                                       : static_cast<double>(exp_cz((ft[j] - mt) * inv_t)) * izt;
-                double r = 0.0;
+                const float a = term(ft[j], mt);
+                float r = 0.0f;
                 if (residual) {
-                    const double b = probs ? static_cast<double>(fd[j]) * izd
-                                           : static_cast<double>(exp_cz((fd[j] - md) * inv_t)) * izd;
-                    const double d = a - b;
-                    r = d > 0.0 ? d : 0.0;
+                    const float d = term(fd[j], md);
+                    // kappa d - a with the product exact in each FMA
+                    const float x = __builtin_fmaf(d, kap_lo, __builtin_fmaf(d, kap_hi, -a));
+                    r = fmaxf(-x, 0.0f);
                 }
                 f(j, a, r);
             }
@@ -604,35 +608,66 @@ struct SampleRows {
 };
 
 // The final-sample masses of one chunk of row pair n (step a5): p and
-// r = max(0, p - q) per element, one mass pair per 1024-element sub-chunk.
+// r = max(0, p - q) per element, one mass pair per 1024-element sub-chunk
+// (one per wave; a sub-chunk past the row's last is not written).  A
+// thread's 16 terms add in fp32, the wave's 64 partial sums in fp64.
 template <typename E, bool kVec>
-__device__ __forceinline__ void chunk_masses(const RejectParams &p, int b, int c, int len, const SeqState &st)
+__device__ __forceinline__ void chunk_masses(const RejectParams &p, int b, int c, const SeqState &st)
 {
-    const SampleRows<E> sr(p, b, len, st);
+    const SampleRows<E> sr(p, b, st.len, st);
     const int v0 = c * kRejChunk + threadIdx.x * kChunkPerThread;
     const int cnt = max(0, min(kChunkPerThread, p.V - v0));
-    double ps = 0.0, rs = 0.0;
-    sr.template visit<kChunkPerThread, kVec>(v0, cnt, [&](int, double a, double r) {
+    float ps = 0.0f, rs = 0.0f;
+    sr.template visit<kChunkPerThread, kVec>(v0, cnt, [&](int, float a, float r) {
         ps += a;
         rs += r;
     });
-    ps = wave_sum(ps);
-    rs = wave_sum(rs);
-    if ((threadIdx.x & 63) == 0)
-        p.cmass[(static_cast<int64_t>(b) * p.nchunks + c) * kSubPerChunk + (threadIdx.x >> 6)] =
-            ChunkMass{rs, ps};
+    const double pm = wave_sum(static_cast<double>(ps) * sr.izt);
+    const double rm = wave_sum(static_cast<double>(rs) * sr.izt);
+    const int sub = c * kSubPerChunk + (threadIdx.x >> 6);
+    if ((threadIdx.x & 63) == 0 && sub < p.nsub)
+        p.cmass[static_cast<int64_t>(b) * p.nsub + sub] = ChunkMass{rm, pm};
 }
 
-// Kernel 3: final-sample masses, one workgroup per (sequence, chunk), on
-// the sequence state of the accept decision: two memory rounds (the state,
-// then both rows' slices).
-template <typename E, bool kVec>
-__global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
+// Kernel 2: the final-sample masses, one workgroup per (sequence, 4096-element
+// chunk).  kDecide (the whole call): wave 0 first takes the sequence's
+// accept decision from the row statistics (the workgroup of chunk 0 also
+// publishes it), then every wave forms the masses of its sub-chunk of row
+// pair n.  Otherwise (a vocabulary shard's masses) the decision comes from
+// the sequence state.
+template <typename E, bool kVec, bool kDecide>
+__device__ __forceinline__ void final_masses(const RejectParams &p)
 {
     const int b = blockIdx.x / p.nchunks;
     const int c = blockIdx.x - b * p.nchunks;
-    const SeqState st = p.seq[b];
-    chunk_masses<E, kVec>(p, b, c, st.len, st);
+    SeqState st;
+    if constexpr (kDecide) {
+        __shared__ SeqState s_st;
+        if (threadIdx.x < 64) {
+            const SeqState d = wave_decide(p, b, c == 0);
+            if (threadIdx.x == 0)
+                s_st = d;
+        }
+        __syncthreads();
+        st = s_st;
+    } else {
+        st = p.seq[b];
+    }
+    chunk_masses<E, kVec>(p, b, c, st);
+}
+
+// 16-byte loads: every wave of the launch fits on the chip at once.
+template <typename E, bool kDecide>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_rej_final(const RejectParams p)
+{
+    final_masses<E, true, kDecide>(p);
+}
+
+// Element loads (rows not made of aligned 16-byte vectors).
+template <typename E, bool kDecide>
+__global__ __launch_bounds__(kThreads) void k_rej_final_scalar(const RejectParams p)
+{
+    final_masses<E, false, kDecide>(p);
 }
 
 // A vocabulary shard's final-sample totals: the sum of its sub-chunk masses
@@ -640,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_chunks(const RejectParams p)
 __global__ __launch_bounds__(kThreads) void k_rej_shard_total(const RejectParams p)
 {
     const int b = blockIdx.x;
-    const int nsub = p.nchunks * kSubPerChunk;
+    const int nsub = p.nsub;
     const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * nsub;
     double r = 0.0, q = 0.0;
     for (int k = threadIdx.x; k < nsub; k += kThreads) {
@@ -655,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_shard_total(const RejectParams
         p.mass_out[b] = ChunkMass{R, P};
 }
 
-// Kernel 4: one workgroup per sequence, two memory rounds.  Round 1 loads
+// Kernel 3: one workgroup per sequence, two memory rounds.  Round 1 loads
 // everything that does not depend on the chosen sub-chunk: the sequence
 // state, u_K, the sequence's sub-chunk masses (kept in registers, and staged
 // in LDS when they fit) and the drafts it re-emits.  Round 2 loads the one
@@ -684,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
             sh[s] = p.shard_mass[static_cast<int64_t>(min(s, p.shard_count - 1)) * p.B + b];
     }
     const float ufin = p.u[static_cast<int64_t>(b) * (K + 1) + K];
-    const int nsub = p.nchunks * kSubPerChunk;
+    const int nsub = p.nsub;
     const ChunkMass *cm = p.cmass + static_cast<int64_t>(b) * nsub;
     const bool staged = nsub <= kSelStage;
     const int per = (nsub + kThreads - 1) / kThreads;      // sub-chunks per thread
@@ -796,8 +831,8 @@ __global__ __launch_bounds__(kThreads) void k_rej_select(const RejectParams p)
     const int cnt = max(0, min(kSubPerThread, p.V - v0));
     double xs[kSubPerThread];
     double own = 0.0;
-    sr.template visit<kSubPerThread, false>(v0, cnt, [&](int j, double a, double r) {
-        xs[j] = use_p ? a : r;
+    sr.template visit<kSubPerThread, false>(v0, cnt, [&](int j, float a, float r) {
+        xs[j] = static_cast<double>(use_p ? a : r) * sr.izt;
         own += xs[j];
     });
     double tot;
@@ -840,15 +875,11 @@ hipError_t launch_typed(const RejectParams &p, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const size_t lds = scan_lds_bytes(p.K, p.segs);
-    hipLaunchKernelGGL(k_rej_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
+    const dim3 g2(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
     if (p.vec_ok)
-        hipLaunchKernelGGL((k_rej_chunks<E, true>), g3, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_rej_final<E, true>), g2, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_rej_chunks<E, false>), g3, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_rej_final_scalar<E, true>), g2, dim3(kThreads), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     hipLaunchKernelGGL((k_rej_select<E, false>), dim3(static_cast<unsigned>(p.B)), dim3(kThreads), 0, s, p);
@@ -883,9 +914,9 @@ hipError_t launch_shard_mass_typed(const RejectParams &p, hipStream_t s)
 {
     const dim3 g3(static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nchunks));
     if (p.vec_ok)
-        hipLaunchKernelGGL((k_rej_chunks<E, true>), g3, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_rej_final<E, false>), g3, dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((k_rej_chunks<E, false>), g3, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_rej_final_scalar<E, false>), g3, dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -908,8 +939,8 @@ hipError_t launch_rejection_shard_stats(const RejectParams &p, int dtype, SoftPa
 
 hipError_t launch_rejection_decide(const RejectParams &p, hipStream_t s)
 {
-    const size_t lds = scan_lds_bytes(p.K, p.segs);
-    hipLaunchKernelGGL(k_rej_scan, dim3(static_cast<unsigned>(p.B)), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL(k_rej_scan, dim3(static_cast<unsigned>((p.B + kWaves - 1) / kWaves)), dim3(kThreads), 0,
+                       s, p);
     return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ namespace sv {
 
 // Elements of one final-sample chunk in rejection sampling (16 per thread of
 // a 256-thread workgroup); each wave's quarter of a chunk (a sub-chunk of
-// 1024 elements) publishes its own masses.
+// 1024 elements, SV_SAMPLE_BLOCK) publishes its own masses.
 constexpr int kRejChunk = 4096;
 constexpr int kRejSub = 1024;
 
@@ -100,6 +100,7 @@ struct RejectParams {
     int32_t B, K, V;
     int32_t segs, seg_len;
     int32_t nchunks;          // ceil(V / kRejChunk)
+    int32_t nsub;             // ceil(V / kRejSub): sub-chunk masses per sequence
     int32_t vec_ok;           // both logit tensors 16-byte aligned, rows a whole
                               // number of 16-byte vectors and V a multiple of
                               // the elements per vector
@@ -145,7 +146,7 @@ struct RejectParams {
     // workspace
     SoftPartial *partial;     // [B*(2K+1)*segs]
     SeqState *seq;            // [B]
-    ChunkMass *cmass;         // [B*nchunks*4] masses per sub-chunk
+    ChunkMass *cmass;         // [B][nsub] masses per sub-chunk
 };
 
 hipError_t launch_rejection(const RejectParams &p, int dtype, hipStream_t s);

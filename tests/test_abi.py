@@ -323,3 +323,65 @@ def test_read_probe_rejects_bad_arguments(lib):
     assert lib.sv_read_probe(FAKE, 1000, FAKE, None) == sv.SV_ERR_INVALID_ARG   # not a multiple of 16
     assert lib.sv_read_probe(FAKE + 4, 1024, FAKE, None) == sv.SV_ERR_INVALID_ARG
     assert lib.sv_read_probe(FAKE, 0, FAKE, None) == sv.SV_ERR_INVALID_ARG
+
+
+def test_tuning_change_between_sizing_and_call(lib):
+    """A call plans from one reading of the tuning: a workspace sized under
+    one setting is either enough for the call under another (the call gets
+    past the workspace check and stops only at the missing device) or
+    rejected with SV_ERR_WORKSPACE -- never accepted and overrun.  The
+    final-sample masses the shard calls hand over sit at the start of the
+    workspace, whatever the setting."""
+    B, K, V = 64, 5, 128256
+    need_default = lib.sv_rejection_workspace_bytes(B, K, V)
+
+    def call(wsb):
+        return lib.sv_verify_rejection(FAKE, FAKE, 1, V, FAKE, None, FAKE, 1.0, B, K, V, FAKE, FAKE,
+                                       None, None, None, None, FAKE, wsb, None)
+    try:
+        assert lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 1 << 16) == 0   # more pieces per row
+        need_more = lib.sv_rejection_workspace_bytes(B, K, V)
+        assert need_more > need_default
+        assert call(need_default) == sv.SV_ERR_WORKSPACE
+        assert call(need_more) not in (sv.SV_OK, sv.SV_ERR_WORKSPACE, sv.SV_ERR_INVALID_ARG)
+        assert lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 64) == 0        # one piece per row
+        need_less = lib.sv_rejection_workspace_bytes(B, K, V)
+        assert need_less < need_default
+        assert call(need_default) not in (sv.SV_OK, sv.SV_ERR_WORKSPACE, sv.SV_ERR_INVALID_ARG)
+        assert call(need_less - 256) == sv.SV_ERR_WORKSPACE
+        # the masses (B * ceil(V / 1024) records of 16 bytes) fit in every plan's workspace
+        masses = B * ((V + 1023) // 1024) * 16
+        assert need_less >= masses and need_more >= masses
+    finally:
+        lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 0)
+    assert lib.sv_rejection_workspace_bytes(B, K, V) == need_default
+
+
+def test_tuning_is_safe_to_change_from_threads(lib):
+    """Setting the tuning while other threads size workspaces: every size
+    returned is one of the sizes a single setting gives."""
+    import threading
+    B, K, V = 64, 5, 128256
+    sizes = set()
+    for w in (512, 2048):
+        lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, w)
+        sizes.add(lib.sv_rejection_workspace_bytes(B, K, V))
+    lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 0)
+    seen = []
+    stop = threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            seen.append(lib.sv_rejection_workspace_bytes(B, K, V))
+    threads = [threading.Thread(target=reader) for _ in range(3)]
+    for t in threads:
+        t.start()
+    try:
+        for i in range(2000):
+            lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 512 if i % 2 else 2048)
+    finally:
+        stop.set()
+        for t in threads:
+            t.join()
+        lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 0)
+    assert seen and set(seen) <= sizes

@@ -107,9 +107,10 @@ def test_tree_partials_equal_unsharded(orc, P):
         np.testing.assert_array_equal(host(got[k]), o[k], err_msg=k)
 
 
-def test_greedy_partials_full_size_eight_shards():
+def test_greedy_partials_full_size_eight_shards(orc):
     """The large greedy workload (B 256, K 8, V 151936, bf16) split into the
-    eight 18992-column shards of an 8-way tensor-parallel output layer."""
+    eight 18992-column shards of an 8-way tensor-parallel output layer: the
+    same results as the oracle on the whole rows, and as the unsharded call."""
     wl = W.greedy_workload(**W.GREEDY_LARGE, seed=W.seed_for(4))
     V = 151936
     shards = [(i * V // 8, (i + 1) * V // 8) for i in range(8)]
@@ -119,6 +120,9 @@ def test_greedy_partials_full_size_eight_shards():
     for a in (0.3, 0.6, 0.9):
         dr = to_dev(wl["drafts"][a])
         got = sv.verify_greedy_partials(parts, dr, V)
+        o = orc.verify_greedy(wl["logits"], wl["drafts"][a])
+        for k in ("accepted", "emitted", "argmax"):
+            np.testing.assert_array_equal(host(got[k]), o[k], err_msg="oracle %s alpha %.1f" % (k, a))
         ref = sv.verify_greedy(lt, dr)
         for k in ("accepted", "emitted", "argmax"):
             np.testing.assert_array_equal(host(got[k]), host(ref[k]), err_msg="%s alpha %.1f" % (k, a))
@@ -237,4 +241,4 @@ def test_rejection_sharded_full_size_eight_shards(orc):
     shards = [(i * V // 8, (i + 1) * V // 8) for i in range(8)]
     _, flagged, mism = _rejection_shard_case(orc, wl, shards, label="full size P8")
     say("sharded rejection full size: flagged %d, mismatched %d of 64" % (flagged, mism))
-    assert mism <= flagged
+    assert flagged <= 4 and mism == 0
