@@ -5,6 +5,7 @@
  *   sv_verify_greedy     greedy verification of K drafts per sequence
  *   sv_verify_rejection  rejection-sampling verification (target p, draft q)
  *   sv_verify_rejection_probs  the same on given probabilities
+ *   sv_verify_rejection_noalloc  the same on the library's own device array
  *   sv_verify_tree       greedy verification of a candidate tree
  *   sv_ngram_propose     n-gram prompt-lookup drafting
  *   sv_suffix_propose    suffix-decoding drafting (context + shared history)
@@ -235,6 +236,33 @@ int sv_verify_rejection_probs(const float *target_probs, const float *draft_prob
                               float *p_draft, float *q_draft,
                               uint32_t *flags, int64_t *stats,
                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sv_verify_rejection_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid hipMalloc): sv_verify_rejection with the same arguments, results
+ * and limits, without a workspace argument.  Its workspace is a device
+ * array of SV_NOALLOC_WORKSPACE_BYTES that the library holds on each GPU it
+ * runs on (loaded with the library's code, kept until the process ends);
+ * the call allocates and frees nothing.  A call whose workspace need
+ * (sv_rejection_workspace_bytes) exceeds the array returns
+ * SV_ERR_UNSUPPORTED before anything is enqueued.  Every call on one GPU
+ * uses that GPU's one array, which keeps the last call's contents (its
+ * final-sample masses, as sv_verify_rejection leaves in its workspace):
+ * calls that can overlap on one GPU -- on different streams, or from other
+ * host threads -- race and must be serialised by the caller.  Nothing in
+ * the array needs clearing between calls: a call writes every byte it reads.
+ */
+#define SV_NOALLOC_WORKSPACE_BYTES (8u << 20)
+
+int sv_verify_rejection_noalloc(const void *target_logits, const void *draft_logits,
+                                int32_t dtype, int64_t row_stride,
+                                const int32_t *draft, const int32_t *draft_len,
+                                const float *uniforms, float temperature,
+                                int32_t B, int32_t K, int32_t V,
+                                int32_t *accepted, int32_t *emitted,
+                                float *p_draft, float *q_draft,
+                                uint32_t *flags, int64_t *stats, void *stream);
 
 /*
  * sv_verify_tree -- [Handbook] "Medusa": candidate continuations form a

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
 SV_F32, SV_BF16 = 0, 1
+NOALLOC_WORKSPACE_BYTES = 8 << 20
 FLAG_DRAFT_OOR, FLAG_BAD_LEN, FLAG_BAD_PARENT = 1, 2, 4
 TUNE_TARGET_WORKGROUPS, TUNE_MIN_SEGMENT_BYTES = 1, 2
 
@@ -34,6 +35,7 @@ TUNE_TARGET_WORKGROUPS, TUNE_MIN_SEGMENT_BYTES = 1, 2
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error_message", "sv_set_tuning",
            "sv_greedy_workspace_bytes", "sv_verify_greedy",
            "sv_rejection_workspace_bytes", "sv_verify_rejection", "sv_verify_rejection_probs",
+           "sv_verify_rejection_noalloc",
            "sv_tree_workspace_bytes", "sv_verify_tree", "sv_ngram_propose",
            "sv_argmax_shard_workspace_bytes", "sv_argmax_shard",
            "sv_verify_greedy_partials", "sv_verify_tree_partials",
@@ -99,6 +101,9 @@ def load(path: str = LIB_PATH):
         L.sv_verify_rejection.restype = ctypes.c_int
         L.sv_verify_rejection.argtypes = [P, P, i32, i64, P, P, P, ctypes.c_float, i32, i32, i32,
                                           P, P, P, P, P, P, P, sz, P]
+        L.sv_verify_rejection_noalloc.restype = ctypes.c_int
+        L.sv_verify_rejection_noalloc.argtypes = [P, P, i32, i64, P, P, P, ctypes.c_float, i32, i32,
+                                                  i32, P, P, P, P, P, P, P]
         L.sv_verify_rejection_probs.restype = ctypes.c_int
         L.sv_verify_rejection_probs.argtypes = [P, P, i64, P, P, P, i32, i32, i32, P, P, P, P, P, P,
                                                 P, sz, P]

@@ -565,6 +565,48 @@ int sv_verify_tree_partials(const sv_argmax_partial *partials, int32_t P,
     return SV_OK;
 }
 
+// ------------------------------------------------------------------ device array
+//
+// The workspace of sv_verify_rejection_noalloc: one array per GPU, loaded
+// with the library's code on that GPU and kept until the process ends, for
+// callers that cannot allocate.  In host code `scratch` only names the
+// symbol; its address on a device comes from hipGetSymbolAddress, taken once
+// per device with that device current (the calling thread's device at the
+// entry point's first call on it), and only that address is passed on.
+
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = SV_NOALLOC_WORKSPACE_BYTES;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The array's address on the current device (after check_device).
+int scratch_for_device(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SV_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return hip_fail(g_scratch_err[dev], "hipGetSymbolAddress of the device array");
+    if (!g_scratch_ptr[dev])
+        return fail(SV_ERR_HIP, "the device array has no address on device %d", dev);
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
+} // namespace
+
 // ------------------------------------------------------------------ rejection
 
 namespace {
@@ -634,7 +676,8 @@ int rejection_call(const void *target_logits, const void *draft_logits,
                    int32_t *accepted, int32_t *emitted,
                    float *p_draft, float *q_draft,
                    uint32_t *flags, int64_t *stats,
-                   void *workspace, size_t workspace_bytes, void *stream, bool probs)
+                   void *workspace, size_t workspace_bytes, void *stream, bool probs,
+                   bool use_scratch = false)
 {
     int st;
     if ((st = check_sizes(B, K, V)) != SV_OK)
@@ -654,12 +697,22 @@ int rejection_call(const void *target_logits, const void *draft_logits,
     const int64_t rows = static_cast<int64_t>(B) * (2 * K + 1);
     const RowPlan pl = plan_items(rows, V, esize_of(dtype), tuning_now());
     const RejLayout L = rej_layout(B, K, V, pl);
-    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
-        return st;
+    if (use_scratch && L.total > kScratchBytes)
+        return fail(SV_ERR_UNSUPPORTED, "this call needs %zu bytes of workspace, above the %zu bytes of the "
+                    "library's device array", L.total, kScratchBytes);
     const int nchunks = (V + sv::kRejChunk - 1) / sv::kRejChunk;
     if ((st = check_grid((rows * pl.segs + 3) / 4)) != SV_OK)
         return st;
     if ((st = check_grid(static_cast<int64_t>(B) * nchunks)) != SV_OK)
+        return st;
+    if (use_scratch) {
+        if ((st = check_device()) != SV_OK)
+            return st;
+        if ((st = scratch_for_device(&workspace)) != SV_OK)
+            return st;
+        workspace_bytes = kScratchBytes;
+    }
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != SV_OK)
         return st;
     if ((st = check_device()) != SV_OK)
         return st;
@@ -722,6 +775,20 @@ int sv_verify_rejection_probs(const float *target_probs, const float *draft_prob
     return rejection_call(target_probs, draft_probs, SV_F32, row_stride, draft, draft_len, uniforms,
                           1.0f, B, K, V, accepted, emitted, p_draft, q_draft, flags, stats,
                           workspace, workspace_bytes, stream, true);
+}
+
+int sv_verify_rejection_noalloc(const void *target_logits, const void *draft_logits,
+                                int32_t dtype, int64_t row_stride,
+                                const int32_t *draft, const int32_t *draft_len,
+                                const float *uniforms, float temperature,
+                                int32_t B, int32_t K, int32_t V,
+                                int32_t *accepted, int32_t *emitted,
+                                float *p_draft, float *q_draft,
+                                uint32_t *flags, int64_t *stats, void *stream)
+{
+    return rejection_call(target_logits, draft_logits, dtype, row_stride, draft, draft_len, uniforms,
+                          temperature, B, K, V, accepted, emitted, p_draft, q_draft, flags, stats,
+                          nullptr, 0, stream, false, true);
 }
 
 // ------------------------------------------------------- rejection, sharded

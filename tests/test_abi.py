@@ -385,3 +385,27 @@ def test_tuning_is_safe_to_change_from_threads(lib):
             t.join()
         lib.sv_set_tuning(sv.TUNE_TARGET_WORKGROUPS, 0)
     assert seen and set(seen) <= sizes
+
+
+def test_noalloc_rejection_size_limit(lib):
+    """The no-allocation rejection call rejects, on the host, a call whose
+    workspace would not fit the library's device array, and validates its
+    arguments like sv_verify_rejection."""
+    B, K, V = 4096, 8, 151936
+    assert lib.sv_rejection_workspace_bytes(B, K, V) > sv.NOALLOC_WORKSPACE_BYTES
+
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, rs=V, draft=FAKE, dl=None, u=FAKE, T=1.0, B=B, K=K, V=V,
+                 acc=FAKE, emi=FAKE)
+        a.update(kw)
+        return lib.sv_verify_rejection_noalloc(a["t"], a["d"], a["dtype"], a["rs"], a["draft"],
+                                               a["dl"], a["u"], a["T"], a["B"], a["K"], a["V"],
+                                               a["acc"], a["emi"], None, None, None, None, None)
+    assert call() == sv.SV_ERR_UNSUPPORTED
+    assert b"device array" in lib.sv_last_error_message()
+    assert call(T=0.0) == sv.SV_ERR_INVALID_ARG
+    assert call(u=None) == sv.SV_ERR_INVALID_ARG
+    assert call(B=0) == sv.SV_ERR_INVALID_ARG
+    # a call that fits gets past the size check (and stops at the missing device here)
+    assert call(B=64, K=5, V=128256, rs=128256) not in (sv.SV_OK, sv.SV_ERR_INVALID_ARG,
+                                                         sv.SV_ERR_WORKSPACE)
