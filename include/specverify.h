@@ -203,7 +203,7 @@ int sv_verify_greedy(const void *logits, int32_t dtype, int64_t row_stride,
  * Limits: 1 <= B, 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= SV_MAX_V.
  */
 #define SV_SAMPLE_BLOCK 1024             /* tokens per final-sample mass record */
-#define SV_SAMPLE_BAND_SCALE 1.9073486328125e-06   /* 16 * 2^-23: final-sample tie band */
+#define SV_SAMPLE_BAND_SCALE 7.152557373046875e-07  /* 6 * 2^-23: final-sample tie band */
 
 size_t sv_rejection_workspace_bytes(int32_t B, int32_t K, int32_t V);
 int sv_verify_rejection(const void *target_logits, const void *draft_logits,
