@@ -43,11 +43,15 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Four tokens at positions pos .. pos+3 of a context row of `stride` ints
 // (pos % 4 == 0), loaded unconditionally: positions outside the row are
 // clamped into it, and the caller never uses them.  kVec: the row is
-// 16-byte aligned and stride % 4 == 0.
-template <bool kVec>
+// 16-byte aligned and stride % 4 == 0.  kKeep: a load whose lines are read
+// again soon allocates in the caches (the halo under a tile is the top of
+// the tile the wave reads next); tiles stream past them.
+template <bool kVec, bool kKeep = false>
 __device__ __forceinline__ i32x4 load4(const int32_t *c, int pos, int stride)
 {
-    if constexpr (kVec) {
+    if constexpr (kVec && kKeep) {
+        return *reinterpret_cast<const i32x4 *>(c + max(0, min(pos, stride - 4)));
+    } else if constexpr (kVec) {
         return __builtin_nontemporal_load(
             reinterpret_cast<const i32x4 *>(c + max(0, min(pos, stride - 4))));
     } else {
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8))) void k
         auto fetch = [&](int i, i32x4 &v, i32x4 &h) {
             const int t = max(tile_of(i), t_bot);
             v = load4<kVec>(c, t * kTile + 4 * lane, stride);
-            h = load4<kVec>(c, t * kTile - kHalo + 4 * (lane & 7), stride);
+            h = load4<kVec, true>(c, t * kTile - kHalo + 4 * (lane & 7), stride);
         };
         i32x4 q[kDepth], hq[kDepth];
 #pragma unroll
