@@ -23,7 +23,9 @@ import threading
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspecverify.so")
+# The library this package loads: the in-tree build, or another build of the
+# same sources named by SPECVERIFY_LIBRARY (e.g. one with sanitized host code).
+LIB_PATH = os.environ.get("SPECVERIFY_LIBRARY") or os.path.join(HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
 SV_F32, SV_BF16 = 0, 1

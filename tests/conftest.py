@@ -22,5 +22,8 @@ def golden(name):
 
 @pytest.fixture(scope="session")
 def orc():
+    """The oracle: the default build, or the build SPECVERIFY_ORACLE names
+    (the sanitizer runs use an instrumented one)."""
     import oracle
-    return oracle.default()
+    path = os.environ.get("SPECVERIFY_ORACLE")
+    return oracle.Oracle(path) if path else oracle.default()
