@@ -10,19 +10,31 @@
 // maximum of the key (min(m(e), n_max) << 26) | e over all e with
 // m(e) >= n_min.
 //
-// kW waves work on one context (kW = 1 for many contexts, so that each
-// wave's in-flight reads are few at its early exit; kW = 4 or 16 for fewer,
-// so that a context is scanned that many tiles at a time: with 16 waves a
-// 8192-token context is in flight in one round).  Wave `sub` scores the
-// 256-position tiles t_top - sub, t_top - sub - kW, ... from the end of the
-// context backwards; each tile comes with the 32 positions below it (the
-// longest comparison's reach), through a ring of kDepth loads per lane, so
-// kDepth - 1 tiles are in flight while one is scored.  A lane holds four
-// consecutive candidate ends and tests their last token against the
-// suffix's last token in registers; only the rare hits compare further,
-// from the tile staged in the wave's LDS.  A wave stops once a full-length
-// (n_max) match is known at or above its next tile, since nothing further
-// back can beat it; the keys' maximum is the answer.
+// A scan: wave by wave, 256-position tiles are read from the end of the
+// context backwards, each with the 32 positions below it (the longest
+// comparison's reach), through a ring of kDepth loads per lane, so kDepth - 1
+// tiles are in flight while one is scored.  A lane holds four consecutive
+// candidate ends and tests their last token against the suffix's last token
+// in registers; only the rare hits compare further, from the tile staged in
+// the wave's LDS.  Once a full-length (n_max) match is known at some tile,
+// no tile below it can beat it, so those are skipped; the keys' maximum is
+// the answer.
+//
+// Two kernels share that scan:
+// - k_ngram, for up to 16383 contexts: kW waves per context (16, one
+//   1024-thread workgroup, for at most 512 contexts, so that a context is
+//   in flight 16 tiles at a time; else 4), wave `sub` taking the tiles
+//   t_top - sub, t_top - sub - kW, ...
+// - k_ngram_groups, for 16384 contexts and more: one round of 1024-thread
+//   workgroups (two per CU), each owning 32 contexts.  A context's tiles
+//   are cut into groups of 16 and the workgroup's 16 waves take groups
+//   from an LDS counter, breadth first (every context's top group, then
+//   every second group, ...).  Measured on 16384 contexts of 8192 tokens,
+//   one wave per context left half the chip's wave slots idle in the
+//   second half of the call: a workgroup's slots are only refilled once
+//   all of its contexts have ended, and a context scanned to the start
+//   takes 32 tiles in series.  With groups every slot stays busy until
+//   the workgroups start to finish.
 
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
@@ -217,6 +229,166 @@ __global__ __launch_bounds__(kWG) __attribute__((amdgpu_waves_per_eu(8))) void k
     }
 }
 
+constexpr int kGroupWaves = 16;            // waves per workgroup of k_ngram_groups
+constexpr int kGroupCtx = 32;              // contexts per workgroup
+constexpr int kGroupTiles = 16;            // tiles per group
+
+template <bool kVec>
+__global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_eu(8))) void k_ngram_groups(const NgramParams p)
+{
+    __shared__ int s_buf[kGroupWaves][kHalo + kTile];
+    __shared__ int s_suf[kGroupCtx][64];          // s_suf[j][i] = c[L-1-i] for i < n_max
+    __shared__ int s_len[kGroupCtx];              // length (0 if invalid), -1 past the batch
+    __shared__ int s_full[kGroupCtx];             // highest tile known to hold a full-length match
+    __shared__ int s_key[kGroupCtx];              // maximum of the groups' keys
+    __shared__ unsigned s_next;                   // 64 x the next group to take
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int stride = static_cast<int>(p.ctx_stride);
+    const int nmax = p.n_max, nmin = p.n_min;
+    const int b0 = blockIdx.x * kGroupCtx;
+    for (int idx = threadIdx.x; idx < kGroupCtx * 64; idx += kGroupWaves * 64) {
+        const int j = idx >> 6, i = idx & 63;
+        const int b = b0 + j;
+        int L = b < p.B ? p.lengths[b] : -1;
+        if (b < p.B && (L < 0 || L > stride))
+            L = 0;                                // flagged with the outputs
+        const int32_t *c = p.tokens + static_cast<int64_t>(b < p.B ? b : 0) * p.ctx_stride;
+        s_suf[j][i] = L > 0 ? c[max(0, L - 1 - min(i, nmax - 1))] : 0;
+        if (i == 0) {
+            s_len[j] = L;
+            s_full[j] = -1;
+            s_key[j] = 0;
+        }
+    }
+    if (threadIdx.x == 0)
+        s_next = 0;
+    __syncthreads();
+
+    const int groups = ((stride + kTile - 1) / kTile + kGroupTiles - 1) / kGroupTiles;
+    const int units = groups * kGroupCtx;
+    int *buf = s_buf[w];
+    for (;;) {
+        // every lane adds 1, so the wave's 64 returns are 64u .. 64u + 63
+        // and u is the same in every lane, with no hand-off between lanes
+        const int u = static_cast<int>(atomicAdd(&s_next, 1u) >> 6);
+        if (u >= units)
+            break;
+        const int j = u % kGroupCtx, g = u / kGroupCtx;
+        const int L = s_len[j];
+        const int e_hi = L - 2, e_lo = nmin - 1;
+        if (L < 0 || e_hi < e_lo)
+            continue;
+        const int t_top = e_hi / kTile, t_bot = e_lo / kTile;
+        const int g_top = t_top - g * kGroupTiles;          // this group: tiles g_top down to g_low
+        const int g_low = max(t_bot, g_top - kGroupTiles + 1);
+        if (g_top < t_bot || s_full[j] >= g_top)
+            continue;
+        const int32_t *c = p.tokens + static_cast<int64_t>(b0 + j) * p.ctx_stride;
+        const int *sfx = s_suf[j];
+        const int s0 = sfx[0];
+        auto fetch = [&](int t, i32x4 &v, i32x4 &h) {
+            t = max(t, g_low);
+            v = load4<kVec>(c, t * kTile + 4 * lane, stride);
+            h = load4<kVec, true>(c, t * kTile - kHalo + 4 * (lane & 7), stride);
+        };
+        i32x4 q[kDepth], hq[kDepth];
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            fetch(g_top - d, q[d], hq[d]);
+        int best = 0;
+        bool stop = false;
+        // as in k_ngram, every ring load is issued on every path
+        for (int r = 0;; r += kDepth) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                const int t = g_top - (r + d);
+                const bool active = !stop && t >= g_low && s_full[j] < t;   // uniform over the wave
+                const i32x4 v = q[d];
+                if (active) {
+                    buf[kHalo + 4 * lane + 0] = v.x;
+                    buf[kHalo + 4 * lane + 1] = v.y;
+                    buf[kHalo + 4 * lane + 2] = v.z;
+                    buf[kHalo + 4 * lane + 3] = v.w;
+                    if (lane < 8) {
+                        const i32x4 h = hq[d];
+                        buf[4 * lane + 0] = h.x;
+                        buf[4 * lane + 1] = h.y;
+                        buf[4 * lane + 2] = h.z;
+                        buf[4 * lane + 3] = h.w;
+                    }
+                }
+                fetch(active ? t - kDepth : t, q[d], hq[d]);
+                if (active) {
+                    const int lo = t * kTile;
+                    const int tok[4] = {v.x, v.y, v.z, v.w};
+                    unsigned hit = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int e = lo + 4 * lane + k;
+                        if (tok[k] == s0 && e >= e_lo && e <= e_hi)
+                            hit |= 1u << k;
+                    }
+                    if (__ballot(hit != 0)) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            if (hit & (1u << k)) {
+                                const int e = lo + 4 * lane + k;
+                                int m = 1;
+                                while (m < nmax && e - m >= 0 &&
+                                       buf[kHalo + 4 * lane + k - m] == sfx[m])
+                                    ++m;
+                                if (m >= nmin)
+                                    best = max(best, (m << kEndBits) | e);
+                            }
+                        }
+                    }
+                    if (__ballot((best >> kEndBits) == nmax)) {
+                        stop = true;
+                        if (lane == 0)
+                            atomicMax(&s_full[j], t);
+                    }
+                } else {
+                    stop = true;
+                }
+            }
+            if (stop)
+                break;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            best = max(best, __shfl_xor(best, off, 64));
+        if (lane == 0 && best > 0)
+            atomicMax(&s_key[j], best);
+    }
+    __syncthreads();
+
+    for (int j = w; j < kGroupCtx; j += kGroupWaves) {
+        const int b = b0 + j;
+        if (b >= p.B)
+            break;
+        const int32_t *c = p.tokens + static_cast<int64_t>(b) * p.ctx_stride;
+        const int Lr = p.lengths[b];
+        const unsigned fl = (Lr < 0 || Lr > stride) ? SV_FLAG_BAD_LEN : 0u;
+        const int L = s_len[j];
+        const int best = s_key[j];
+        const int n = best >> kEndBits;
+        const int e = best & ((1 << kEndBits) - 1);
+        const int m = n > 0 ? min(p.K, L - 1 - e) : 0;
+        for (int k = lane; k < p.K; k += 64)
+            p.proposal[static_cast<int64_t>(b) * p.K + k] = k < m ? c[e + 1 + k] : -1;
+        if (lane == 0) {
+            p.proposal_len[b] = m;
+            if (p.match_n)
+                p.match_n[b] = n;
+            if (p.match_pos)
+                p.match_pos[b] = n > 0 ? e - n + 1 : -1;
+            if (p.flags)
+                p.flags[b] = fl;
+        }
+    }
+}
+
 template <bool kVec, int kW, int kWG>
 hipError_t launch_w(const NgramParams &p, hipStream_t s)
 {
@@ -230,15 +402,21 @@ hipError_t launch_w(const NgramParams &p, hipStream_t s)
 
 hipError_t launch_ngram(const NgramParams &p, hipStream_t s)
 {
-    // one wave per context once the contexts alone fill the chip's wave slots
-    // (256 CUs x 32) twice; four waves per context below that, and sixteen
-    // (one 1024-thread workgroup) for a batch of at most 512 contexts
-    const bool many = p.B >= 2 * 256 * 32, few = p.B <= 512;
+    // 16384 contexts (32 per workgroup, two workgroups per CU) fill the chip
+    // in one round; below that, sixteen waves per context (one 1024-thread
+    // workgroup) for at most 512 contexts, four otherwise
+    if (p.B >= 2 * 256 * kGroupCtx) {
+        const dim3 grid(static_cast<unsigned>((p.B + kGroupCtx - 1) / kGroupCtx));
+        if (p.vec_ok)
+            hipLaunchKernelGGL((k_ngram_groups<true>), grid, dim3(kGroupWaves * 64), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_ngram_groups<false>), grid, dim3(kGroupWaves * 64), 0, s, p);
+        return hipGetLastError();
+    }
+    const bool few = p.B <= 512;
     if (p.vec_ok)
-        return many ? launch_w<true, 1, kThreads>(p, s)
-                    : (few ? launch_w<true, 16, 1024>(p, s) : launch_w<true, 4, kThreads>(p, s));
-    return many ? launch_w<false, 1, kThreads>(p, s)
-                : (few ? launch_w<false, 16, 1024>(p, s) : launch_w<false, 4, kThreads>(p, s));
+        return few ? launch_w<true, 16, 1024>(p, s) : launch_w<true, 4, kThreads>(p, s);
+    return few ? launch_w<false, 16, 1024>(p, s) : launch_w<false, 4, kThreads>(p, s);
 }
 
 } // namespace sv

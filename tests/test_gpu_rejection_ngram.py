@@ -193,6 +193,44 @@ def test_ngram_bandwidth_size_sampled(orc):
     _ngram_case(orc, wl["tokens"], wl["lengths"], 2, 5, 8, "B16384")
 
 
+def test_ngram_many_contexts_ragged(orc):
+    """The grouped kernel (16384 contexts and more, 32 per workgroup, tiles in
+    groups of 16): a batch that leaves the last workgroup part-filled,
+    ragged and invalid lengths, rows of 20 tiles (two groups, the second
+    short), long planted repeats, Zipf ids from a small vocabulary so that
+    matches of every length occur; element loads (stride % 4 != 0) and
+    16-byte loads."""
+    rng = np.random.default_rng(20261203)
+    B, stride = 16384 + 37, 5003
+    tokens = W.zipf_tokens(rng, (B, stride), 3000, 1.1).astype(np.int32)
+    lengths = rng.integers(0, stride + 1, B).astype(np.int32)
+    lengths[rng.random(B) < 0.3] = stride
+    lengths[[5, 77, B - 1]] = [-1, stride + 1, -7]
+    for b in range(0, B, 5):               # long repeats at every depth
+        L = int(lengths[b])
+        if L > 200:
+            n = int(rng.integers(8, 40))
+            s0 = int(rng.integers(0, L - n))
+            tokens[b, L - n:L] = tokens[b, s0:s0 + n]
+    for n_min, n_max, K in [(2, 5, 8), (1, 31, 16), (3, 3, 70)]:
+        _ngram_case(orc, tokens, lengths, n_min, n_max, K, "many ragged n%d-%d" % (n_min, n_max))
+    aligned = np.zeros((B, 5004), np.int32)
+    aligned[:, :stride] = tokens
+    _ngram_case(orc, aligned, np.clip(lengths, -1, 5004), 2, 5, 8, "many aligned")
+
+
+def test_ngram_many_contexts_short_rows(orc):
+    """The grouped kernel on rows of one tile and less: every context's only
+    group, contexts too short for n_min, and the empty context."""
+    rng = np.random.default_rng(7)
+    B, stride = 20000, 200
+    tokens = rng.integers(0, 6, (B, stride)).astype(np.int32)
+    lengths = rng.integers(0, stride + 1, B).astype(np.int32)
+    lengths[:64] = np.arange(64)
+    for n_min, n_max, K in [(1, 4, 5), (4, 31, 3)]:
+        _ngram_case(orc, tokens, lengths, n_min, n_max, K, "many short n%d-%d" % (n_min, n_max))
+
+
 def test_ngram_exhaustive_ternary(orc):
     """Every context in {0,1,2}^L, L <= 9, at one stride (ragged lengths),
     for several lookup ranges and K."""
