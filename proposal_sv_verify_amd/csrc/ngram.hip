@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
     __shared__ int s_full[kGroupCtx];             // highest tile known to hold a full-length match
     __shared__ int s_key[kGroupCtx];              // maximum of the groups' keys
     __shared__ unsigned s_next;                   // 64 x the next group to take
+    __shared__ int s_tiles;                       // most candidate tiles of any context here
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int stride = static_cast<int>(p.ctx_stride);
@@ -261,11 +262,19 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
             s_key[j] = 0;
         }
     }
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         s_next = 0;
+        s_tiles = 0;
+    }
+    __syncthreads();
+    if (threadIdx.x < kGroupCtx) {                // the groups come from the contexts' lengths,
+        const int L = s_len[threadIdx.x];         // not the row stride
+        if (L - 2 >= nmin - 1)
+            atomicMax(&s_tiles, (L - 2) / kTile - (nmin - 1) / kTile + 1);
+    }
     __syncthreads();
 
-    const int groups = ((stride + kTile - 1) / kTile + kGroupTiles - 1) / kGroupTiles;
+    const int groups = (s_tiles + kGroupTiles - 1) / kGroupTiles;
     const int units = groups * kGroupCtx;
     int *buf = s_buf[w];
     for (;;) {

@@ -229,6 +229,12 @@ def test_ngram_many_contexts_short_rows(orc):
     lengths[:64] = np.arange(64)
     for n_min, n_max, K in [(1, 4, 5), (4, 31, 3)]:
         _ngram_case(orc, tokens, lengths, n_min, n_max, K, "many short n%d-%d" % (n_min, n_max))
+    # short contexts in long rows: the groups follow the lengths, not the stride
+    B, stride = 16384, 4096
+    tokens = rng.integers(0, 20, (B, stride)).astype(np.int32)
+    lengths = rng.integers(0, 700, B).astype(np.int32)
+    lengths[::997] = stride
+    _ngram_case(orc, tokens, lengths, 2, 6, 4, "many short in long rows")
 
 
 def test_ngram_exhaustive_ternary(orc):
