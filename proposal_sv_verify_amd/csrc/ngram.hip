@@ -29,7 +29,9 @@
 //   workgroups (two per CU), each owning 32 contexts.  A context's tiles
 //   are cut into groups of 16 and the workgroup's 16 waves take groups
 //   from an LDS counter, breadth first (every context's top group, then
-//   every second group, ...).  Measured on 16384 contexts of 8192 tokens,
+//   every second group, ...).  Within a group a tile is scored one step
+//   after it is staged: the next tile down, staged meanwhile, supplies its
+//   halo, so only the group's bottom tile needs a halo load of its own.  Measured on 16384 contexts of 8192 tokens,
 //   one wave per context left half the chip's wave slots idle in the
 //   second half of the call: a workgroup's slots are only refilled once
 //   all of its contexts have ended, and a context scanned to the start
@@ -236,7 +238,7 @@ constexpr int kGroupTiles = 16;            // tiles per group
 template <bool kVec>
 __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_eu(8))) void k_ngram_groups(const NgramParams p)
 {
-    __shared__ int s_buf[kGroupWaves][kHalo + kTile];
+    __shared__ int s_buf[kGroupWaves][2][kHalo + kTile];   // two tiles per wave, each with its halo
     __shared__ int s_suf[kGroupCtx][64];          // s_suf[j][i] = c[L-1-i] for i < n_max
     __shared__ int s_len[kGroupCtx];              // length (0 if invalid), -1 past the batch
     __shared__ int s_full[kGroupCtx];             // highest tile known to hold a full-length match
@@ -276,7 +278,8 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
 
     const int groups = (s_tiles + kGroupTiles - 1) / kGroupTiles;
     const int units = groups * kGroupCtx;
-    int *buf = s_buf[w];
+    int *buf0 = s_buf[w][0];
+    int *buf1 = s_buf[w][1];
     for (;;) {
         // every lane adds 1, so the wave's 64 returns are 64u .. 64u + 63
         // and u is the same in every lane, with no hand-off between lanes
@@ -296,56 +299,64 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
         const int32_t *c = p.tokens + static_cast<int64_t>(b0 + j) * p.ctx_stride;
         const int *sfx = s_suf[j];
         const int s0 = sfx[0];
-        auto fetch = [&](int t, i32x4 &v, i32x4 &h) {
-            t = max(t, g_low);
-            v = load4<kVec>(c, t * kTile + 4 * lane, stride);
-            h = load4<kVec, true>(c, t * kTile - kHalo + 4 * (lane & 7), stride);
+        const int n = g_top - g_low + 1;                    // tiles in the group
+        // step s of the ring: tile g_top - s for s < n; past the bottom tile,
+        // the 32 positions under it (its halo; lanes 0..7 hold them)
+        auto fetch = [&](int st) {
+            const int pos = st < n ? (g_top - st) * kTile + 4 * lane : g_low * kTile - kHalo + 4 * (lane & 7);
+            return load4<kVec>(c, pos, stride);
         };
-        i32x4 q[kDepth], hq[kDepth];
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d)
-            fetch(g_top - d, q[d], hq[d]);
+        i32x4 q0 = fetch(0), q1 = fetch(1), pv = q0;
         int best = 0;
         bool stop = false;
-        // as in k_ngram, every ring load is issued on every path
-        for (int r = 0;; r += kDepth) {
-#pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
-                const int t = g_top - (r + d);
-                const bool active = !stop && t >= g_low && s_full[j] < t;   // uniform over the wave
-                const i32x4 v = q[d];
-                if (active) {
-                    buf[kHalo + 4 * lane + 0] = v.x;
-                    buf[kHalo + 4 * lane + 1] = v.y;
-                    buf[kHalo + 4 * lane + 2] = v.z;
-                    buf[kHalo + 4 * lane + 3] = v.w;
-                    if (lane < 8) {
-                        const i32x4 h = hq[d];
-                        buf[4 * lane + 0] = h.x;
-                        buf[4 * lane + 1] = h.y;
-                        buf[4 * lane + 2] = h.z;
-                        buf[4 * lane + 3] = h.w;
+        // Step k stages tile k (its top 32 positions also become the halo of
+        // tile k - 1, staged one step earlier) and then scores tile k - 1,
+        // whose halo is now complete; after the last tile, step n stages the
+        // bottom tile's halo from the extra load and scores it.
+        auto step = [&](int k, i32x4 &qs, int *bs, int *bo) {
+            const i32x4 v = qs;
+            if (!stop) {
+                if (k < n) {
+                    bs[kHalo + 4 * lane + 0] = v.x;
+                    bs[kHalo + 4 * lane + 1] = v.y;
+                    bs[kHalo + 4 * lane + 2] = v.z;
+                    bs[kHalo + 4 * lane + 3] = v.w;
+                    if (k >= 1 && lane >= 56) {
+                        bo[4 * (lane - 56) + 0] = v.x;
+                        bo[4 * (lane - 56) + 1] = v.y;
+                        bo[4 * (lane - 56) + 2] = v.z;
+                        bo[4 * (lane - 56) + 3] = v.w;
                     }
+                } else if (lane < 8) {
+                    bo[4 * lane + 0] = v.x;
+                    bo[4 * lane + 1] = v.y;
+                    bo[4 * lane + 2] = v.z;
+                    bo[4 * lane + 3] = v.w;
                 }
-                fetch(active ? t - kDepth : t, q[d], hq[d]);
-                if (active) {
+            }
+            qs = fetch(min(k + 2, n));
+            if (!stop && k >= 1) {
+                const int t = g_top - (k - 1);
+                if (s_full[j] >= t) {
+                    stop = true;
+                } else {
                     const int lo = t * kTile;
-                    const int tok[4] = {v.x, v.y, v.z, v.w};
+                    const int tok[4] = {pv.x, pv.y, pv.z, pv.w};
                     unsigned hit = 0;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int e = lo + 4 * lane + k;
-                        if (tok[k] == s0 && e >= e_lo && e <= e_hi)
-                            hit |= 1u << k;
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int e = lo + 4 * lane + kk;
+                        if (tok[kk] == s0 && e >= e_lo && e <= e_hi)
+                            hit |= 1u << kk;
                     }
                     if (__ballot(hit != 0)) {
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            if (hit & (1u << k)) {
-                                const int e = lo + 4 * lane + k;
+                        for (int kk = 0; kk < 4; ++kk) {
+                            if (hit & (1u << kk)) {
+                                const int e = lo + 4 * lane + kk;
                                 int m = 1;
                                 while (m < nmax && e - m >= 0 &&
-                                       buf[kHalo + 4 * lane + k - m] == sfx[m])
+                                       bo[kHalo + 4 * lane + kk - m] == sfx[m])
                                     ++m;
                                 if (m >= nmin)
                                     best = max(best, (m << kEndBits) | e);
@@ -357,10 +368,15 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
                         if (lane == 0)
                             atomicMax(&s_full[j], t);
                     }
-                } else {
-                    stop = true;
                 }
             }
+            pv = v;
+            if (k >= n)
+                stop = true;
+        };
+        for (int k = 0;; k += 2) {
+            step(k, q0, buf0, buf1);
+            step(k + 1, q1, buf1, buf0);
             if (stop)
                 break;
         }
