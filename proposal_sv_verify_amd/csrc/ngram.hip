@@ -282,19 +282,21 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
     int *buf1 = s_buf[w][1];
     for (;;) {
         // every lane adds 1, so the wave's 64 returns are 64u .. 64u + 63
-        // and u is the same in every lane, with no hand-off between lanes
-        const int u = static_cast<int>(atomicAdd(&s_next, 1u) >> 6);
+        // and u is the same in every lane, with no hand-off between lanes;
+        // reading it (and the LDS words below) as wave-uniform values lets
+        // the group's control flow run on scalar branches
+        const int u = __builtin_amdgcn_readfirstlane(static_cast<int>(atomicAdd(&s_next, 1u) >> 6));
         if (u >= units)
             break;
         const int j = u % kGroupCtx, g = u / kGroupCtx;
-        const int L = s_len[j];
+        const int L = __builtin_amdgcn_readfirstlane(s_len[j]);
         const int e_hi = L - 2, e_lo = nmin - 1;
         if (L < 0 || e_hi < e_lo)
             continue;
         const int t_top = e_hi / kTile, t_bot = e_lo / kTile;
         const int g_top = t_top - g * kGroupTiles;          // this group: tiles g_top down to g_low
         const int g_low = max(t_bot, g_top - kGroupTiles + 1);
-        if (g_top < t_bot || s_full[j] >= g_top)
+        if (g_top < t_bot || __builtin_amdgcn_readfirstlane(s_full[j]) >= g_top)
             continue;
         const int32_t *c = p.tokens + static_cast<int64_t>(b0 + j) * p.ctx_stride;
         const int *sfx = s_suf[j];
@@ -337,17 +339,19 @@ __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_e
             qs = fetch(min(k + 2, n));
             if (!stop && k >= 1) {
                 const int t = g_top - (k - 1);
-                if (s_full[j] >= t) {
+                if (__builtin_amdgcn_readfirstlane(s_full[j]) >= t) {
                     stop = true;
                 } else {
                     const int lo = t * kTile;
-                    const int tok[4] = {pv.x, pv.y, pv.z, pv.w};
-                    unsigned hit = 0;
+                    unsigned hit = static_cast<unsigned>(pv.x == s0) | (static_cast<unsigned>(pv.y == s0) << 1) |
+                                   (static_cast<unsigned>(pv.z == s0) << 2) | (static_cast<unsigned>(pv.w == s0) << 3);
+                    if (lo < e_lo || lo + kTile - 1 > e_hi) {     // a tile at either end of the range
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const int e = lo + 4 * lane + kk;
-                        if (tok[kk] == s0 && e >= e_lo && e <= e_hi)
-                            hit |= 1u << kk;
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const int e = lo + 4 * lane + kk;
+                            if (e < e_lo || e > e_hi)
+                                hit &= ~(1u << kk);
+                        }
                     }
                     if (__ballot(hit != 0)) {
 #pragma unroll
