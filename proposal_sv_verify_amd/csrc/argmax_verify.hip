@@ -67,12 +67,13 @@ __global__ __launch_bounds__(kThreads) void k_row_argmax(const ArgVerifyParams p
 // Row argmax from its segment partials.  A row whose elements all compare
 // false against -inf keeps the sentinel; id 0 is then the lowest id holding
 // the maximum.
-__device__ __forceinline__ int merged_argmax(const ArgVerifyParams &p, int64_t row)
+__device__ __forceinline__ int merged_argmax(const ArgVerifyParams &p, int64_t row, const ArgPartial &q0)
 {
     const ArgPartial *pp = p.partial_in + row * p.part_row_step;
     float bv = -__builtin_inff();
     int bi = kIdxNone;
-    for (int s = 0; s < p.segs; ++s) {
+    arg_combine(bv, bi, q0.v, q0.i);
+    for (int s = 1; s < p.segs; ++s) {
         const ArgPartial q = pp[s * p.part_seg_step];
         arg_combine(bv, bi, q.v, q.i);
     }
@@ -110,12 +111,17 @@ __global__ __launch_bounds__(kThreads) void k_greedy_scan(const ArgVerifyParams 
     bool oor = false;
     for (int base = 0; base <= K; base += 64) {
         const int i = base + lane;
+        // both loads first (indices clamped onto existing entries), so that
+        // they travel in one round: the row's first partial and the draft
+        const int64_t row = static_cast<int64_t>(b) * (K + 1) + min(i, K);
+        const ArgPartial q0 = p.partial_in[row * p.part_row_step];
+        const int xr = K > 0 ? d[max(0, min(i, K - 1))] : 0;
         int t = -1;
         if (i <= len)
-            t = merged_argmax(p, static_cast<int64_t>(b) * (K + 1) + i);
+            t = merged_argmax(p, row, q0);
         if (p.argmax_out && i <= K)
             p.argmax_out[static_cast<int64_t>(b) * (K + 1) + i] = t;
-        const int x = i < len ? d[i] : 0;
+        const int x = i < len ? xr : 0;
         if (i < len && (x < 0 || x >= p.V))
             oor = true;
         const unsigned long long mism = __ballot(i < len && x != t);
@@ -180,10 +186,15 @@ __global__ __launch_bounds__(kThreads) void k_tree_scan(const ArgVerifyParams p)
         s_fl = 0;
     for (int j = threadIdx.x; j < N; j += kThreads) {
         const int64_t o = static_cast<int64_t>(b) * N + j;
-        const int t = merged_argmax(p, o);
+        // the three loads first, so that they travel in one round
+        const ArgPartial q0 = p.partial_in[o * p.part_row_step];
+        const int par = p.parent[o];
+        const int tok = p.token[o];
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = merged_argmax(p, o, q0);
         s_t[j] = t;
-        s_par[j] = p.parent[o];
-        s_tok[j] = p.token[o];
+        s_par[j] = par;
+        s_tok[j] = tok;
         if (p.argmax_out)
             p.argmax_out[o] = t;
     }
