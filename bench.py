@@ -607,7 +607,7 @@ def main():
     ap.add_argument("--no-suffix", action="store_true",
                     help="skip the suffix-decoding proposer measurement")
     ap.add_argument("--no-graph", action="store_true",
-                    help="skip the HIP-graph replay of the step and of a small-batch step")
+                    help="skip the alternative step executions: HIP-graph replay (of the step and of a small-batch step) and the four-stream step")
     ap.add_argument("--no-greedy-extra", action="store_true",
                     help="skip the small greedy workload and the acceptance-rate sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -670,13 +670,13 @@ def main():
         for k in kernels.values():
             k["frac_of_measured_ceiling"] = round(k["gb_per_s"] / ceil["read_gb_per_s"], 4)
         roofline["frac_of_measured_ceiling"] = round(achieved / ceil["read_gb_per_s"], 4)
-    result["step_concurrent"] = concurrent_step(dev_inputs, outs, K, positions)
     if not args.no_bandwidth_mode:
         result["ngram_bandwidth_mode"] = ngram_bandwidth_mode(args)
     if not args.no_suffix:
         result["suffix_proposer"] = suffix_proposer()
     if not args.no_graph:
         result["graph_step"] = graph_steps(dev_inputs)
+        result["step_concurrent"] = concurrent_step(dev_inputs, outs, K, positions)
     if not args.no_greedy_extra:
         result["greedy_small"] = greedy_small()
         result["greedy_alphas"] = greedy_alphas(gr)
