@@ -113,6 +113,19 @@ def test_rejection_extreme_logits(orc, case, dtype):
     _rej_case(orc, wl, label="extreme %s %s" % (case, dtype))
 
 
+@pytest.mark.parametrize("T", [0.05, 0.12, 8.0, 50.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rejection_extreme_temperatures(orc, T, dtype):
+    """Temperatures far from 1: at T = 0.05 the terms of N(0, 2) logits
+    reach e^±160, far outside fp32 against a zero reference (the careful
+    path), and at large T the rows are nearly flat.  Drafts are sampled at
+    the same temperature."""
+    wl = W.rejection_workload(16, 4, 30011, 2.0, 0.5, T, seed=int(T * 1000) + (7 if dtype == "f32" else 0),
+                              dtype=dtype)
+    flagged, mism = _rej_case(orc, wl, label="T%g %s" % (T, dtype), max_flagged=2)
+    assert mism == 0
+
+
 @pytest.mark.parametrize("K", [63, 64, 130])
 def test_rejection_long_drafts(orc, K):
     """Draft lengths at and past one 64-position block of the accept scan
