@@ -409,3 +409,48 @@ def test_noalloc_rejection_size_limit(lib):
     # a call that fits gets past the size check (and stops at the missing device here)
     assert call(B=64, K=5, V=128256, rs=128256) not in (sv.SV_OK, sv.SV_ERR_INVALID_ARG,
                                                          sv.SV_ERR_WORKSPACE)
+
+
+C_PROGRAM = r"""
+#include "specverify.h"
+#include <stdio.h>
+
+int main(void)
+{
+    const int32_t tiers[3] = {1, 3, 7};
+    sv_adaptive st;
+    printf("%d %s\n", sv_abi_version(), sv_status_string(SV_ERR_INVALID_ARG));
+    printf("%d\n", sv_greedy_workspace_bytes(4, 4, 32000) > 0);
+    printf("%d\n", sv_rejection_workspace_bytes(64, 5, 128256) > 0);
+    printf("%d\n", sv_verify_greedy(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) == SV_ERR_INVALID_ARG);
+    if (sv_adaptive_init(&st, tiers, 3, 0.5, 0.0) != SV_OK)
+        return 1;
+    sv_adaptive_update(&st, 2.0);
+    printf("%d %.2f\n", st.k, st.ema);
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c99_and_links(lib, tmp_path):
+    """The boundary is a C ABI: the header compiles as strict C99 with every
+    warning an error, and a C program links against the library and calls
+    the host-side entry points (version, status strings, workspace sizes,
+    argument validation, the adaptive controller); nothing here needs a GPU."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    # the library by path (a sanitizer build has another name, and its
+    # runtime symbols come from a preloaded library)
+    libdir = os.path.dirname(os.path.abspath(sv.LIB_PATH))
+    subprocess.check_call([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                           os.path.dirname(HEADER), str(src), os.path.abspath(sv.LIB_PATH),
+                           "-Wl,-rpath," + libdir, "-Wl,--allow-shlib-undefined", "-o", str(exe)])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    assert out[0] == "%d SV_ERR_INVALID_ARG" % lib.sv_abi_version()
+    assert out[1:4] == ["1", "1", "1"]
+    assert out[4] == "3 1.00"                  # ema 0.5 * 2 = 1; smallest tier >= 2 * 1 is 3
