@@ -250,6 +250,31 @@ def test_ngram_many_contexts_short_rows(orc):
     _ngram_case(orc, tokens, lengths, 2, 6, 4, "many short in long rows")
 
 
+def test_full_size_calls_repeat_bit_identically():
+    """Run-twice identity at full size, the launch shapes with the most
+    workgroups and the LDS atomic combines: rejection sampling (2048
+    final-sample workgroups; p and q compared as bits) and the grouped
+    n-gram kernel (16384 contexts, group claims and key maxima in LDS)."""
+    wl = W.rejection_workload(**W.REJECTION, seed=W.seed_for(3, salt=2))
+    t, d = to_dev(wl["target"]), to_dev(wl["draft_logits"])
+    x, u = to_dev(wl["draft"]), to_dev(wl["uniforms"])
+    first = {k: host(v) for k, v in sv.verify_rejection(t, d, x, u).items()}
+    for _ in range(2):
+        again = sv.verify_rejection(t, d, x, u)
+        for k in first:
+            np.testing.assert_array_equal(host(again[k]).view(np.uint32) if first[k].dtype == np.float32
+                                          else host(again[k]),
+                                          first[k].view(np.uint32) if first[k].dtype == np.float32 else first[k],
+                                          err_msg="rejection repeat %s" % k)
+    ng = W.ngram_workload(16384, 8192, seed=W.seed_for(2, salt=4))
+    tok, lens = to_dev(ng["tokens"]), to_dev(ng["lengths"])
+    first = {k: host(v) for k, v in sv.ngram_propose(tok, lens, 2, 5, 8).items()}
+    for _ in range(2):
+        again = sv.ngram_propose(tok, lens, 2, 5, 8)
+        for k in first:
+            np.testing.assert_array_equal(host(again[k]), first[k], err_msg="ngram repeat %s" % k)
+
+
 def test_ngram_exhaustive_ternary(orc):
     """Every context in {0,1,2}^L, L <= 9, at one stride (ragged lengths),
     for several lookup ranges and K."""
